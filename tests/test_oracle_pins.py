@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against what the source pages and mathematics fix.
+
+None of these tests re-derives the oracle's own formulas: they use hand-worked
+examples (tests/golden), closed forms, brute force over all quantization
+levels, independent library routines (torch's affine quantizer and min/max
+observer), exact invariants, and an independent Jacobi eigen-solver.
+Citations: "[TTQ §method bN]" = bullet N of the "proposed method" section of
+the TTQ review page; "[TTQ §results rN]" = bullet N of its key-results section.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import load_golden
+from online_activation_aware_amd import synth
+
+
+def _bf16(a):
+    return synth.f64_to_bf16_bits(np.asarray(a, dtype=np.float64))
+
+
+# ----------------------------------------------------------------- stats
+
+def test_stats_closed_form_plus_minus_a():
+    # [TTQ §method b2-b3]: channel j holding +-a_j in every token has
+    # second moment a_j^2, so ssq_j = T a_j^2 exactly (dyadic a_j).
+    rng = np.random.default_rng(0)
+    T, K = 37, 24
+    a = rng.integers(1, 64, size=K) / 8.0
+    signs = rng.choice([-1.0, 1.0], size=(T, K))
+    X = signs * a[None, :]
+    for dt in ("f32", "bf16"):
+        Xe = synth.encode(X, dt)
+        np.testing.assert_array_equal(oracle.stats(Xe, dt), T * a * a)
+
+
+def test_stats_brute_force_loops():
+    rng = np.random.default_rng(1)
+    T, K = 9, 7
+    X = synth.encode(rng.standard_normal((T, K)) * 3, "f32")
+    got = oracle.stats(X, "f32")
+    for j in range(K):
+        acc = 0.0
+        for t in range(T):
+            x = float(X[t, j])
+            acc += x * x
+        assert got[j] == pytest.approx(acc, rel=1e-14)
+
+
+def test_stats_chunks_accumulate():
+    rng = np.random.default_rng(2)
+    X = _bf16(rng.integers(-50, 50, size=(40, 16)))  # integers: all sums exact
+    whole = oracle.stats(X, "bf16")
+    part = oracle.stats(X[25:], "bf16", oracle.stats(X[:25], "bf16"))
+    np.testing.assert_array_equal(whole, part)
+
+
+# ----------------------------------------------------------------- scales
+
+def test_scales_hand_example():
+    g = load_golden("scales_hand_example.json")
+    X = synth.encode(np.array(g["X"]), "f32")
+    ssq = oracle.stats(X, "f32")
+    np.testing.assert_array_equal(ssq, g["ssq"])
+    s = oracle.awq_scales(ssq, len(g["X"]), g["alpha"], g["lambda_rel"])
+    assert s.dtype == np.float32
+    np.testing.assert_allclose(s.astype(np.float64), g["s"], rtol=g["rtol"])
+
+
+def test_scales_alpha_zero_is_one():
+    # alpha = 0 removes activation awareness: plain RTN ([TTQ §results] baseline)
+    rng = np.random.default_rng(3)
+    ssq = rng.random(64) * 100
+    ssq[5] = 0.0
+    s = oracle.awq_scales(ssq, 10, 0.0, 1e-2)
+    np.testing.assert_array_equal(s, np.ones(64, np.float32))
+
+
+def test_scales_all_zero_input_defined_as_one():
+    s = oracle.awq_scales(np.zeros(32), 8, 0.5, 1e-2)
+    np.testing.assert_array_equal(s, np.ones(32, np.float32))
+    # lambda_rel = 0 and a dead channel: c + lambda == 0 only there
+    s = oracle.awq_scales(np.array([0.0, 4.0]), 1, 0.5, 0.0)
+    assert s[0] == 1.0 and s[1] == pytest.approx(math.sqrt(2.0), rel=1e-7)
+
+
+def test_scales_monotone_and_power_law():
+    rng = np.random.default_rng(4)
+    ssq = np.sort(rng.random(200) * 50)
+    s = oracle.awq_scales(ssq, 7, 0.5, 1e-2).astype(np.float64)
+    assert np.all(np.diff(s) >= 0)
+    # scaling X by 2 scales c and lambda by 4, hence s by 4^(alpha/2) = 2^alpha
+    for alpha in (0.5, 1.0, 0.25):
+        s1 = oracle.awq_scales(ssq, 7, alpha, 1e-2).astype(np.float64)
+        s2 = oracle.awq_scales(4.0 * ssq, 7, alpha, 1e-2).astype(np.float64)
+        np.testing.assert_allclose(s2, s1 * 2.0 ** alpha, rtol=2e-7)
+
+
+def test_scales_p_other_than_two_rejected():
+    with pytest.raises(NotImplementedError):
+        oracle.awq_scales(np.ones(4), 1, 0.5, 1e-2, p=1.0)
+
+
+# ----------------------------------------------------------- quantization
+
+def test_rtn_hand_example():
+    g = load_golden("rtn_hand_example.json")
+    v = np.array([g["v"]], dtype=np.float32)
+    r = oracle.group_rtn(v, g["bits"], g["group"])
+    np.testing.assert_array_equal(r["q"][0], g["q"])
+    np.testing.assert_array_equal(r["delta"][0].astype(np.float64), g["delta"])
+    np.testing.assert_array_equal(r["zero"][0].astype(np.float64), g["zero"])
+    words = oracle.pack_codes(r["q"], g["bits"]).view(np.uint32)[0]
+    assert [f"{int(w):08X}" for w in words] == g["words_hex"]
+    w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], g["group"])[0]
+    np.testing.assert_array_equal(w_hat, g["w_hat"])
+    # the same example through the weight-and-scale entry (s = 1)
+    v2 = oracle.quant_values(synth.encode(np.array([g["v"]]), "f32"), "f32", np.ones(16, np.float32))
+    np.testing.assert_array_equal(v2, v)
+
+
+def test_pack_three_bit_straddle_hand_example():
+    g = load_golden("pack3_hand_example.json")
+    q = np.zeros((1, g["K"]), dtype=np.int64)
+    for j, c in g["codes_nonzero"].items():
+        q[0, int(j)] = c
+    words = oracle.pack_codes(q, g["bits"]).view(np.uint32)[0]
+    assert [f"{int(w):08X}" for w in words] == g["words_hex"]
+    np.testing.assert_array_equal(oracle.unpack_codes(oracle.pack_codes(q, 3), 3, g["K"]), q)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_pack_roundtrip_and_bit_positions(bits):
+    rng = np.random.default_rng(10 + bits)
+    M, K = 5, 128
+    q = rng.integers(0, 2 ** bits, size=(M, K))
+    packed = oracle.pack_codes(q, bits)
+    assert packed.dtype == np.int32 and packed.shape == (M, K * bits // 32)
+    np.testing.assert_array_equal(oracle.unpack_codes(packed, bits, K), q)
+    # independent bit addressing: stream bit (b*j + i) is bit i of code j
+    words = packed.view(np.uint32)
+    for (o, j) in [(0, 0), (1, 31), (2, 77), (4, 127), (3, 10)]:
+        for i in range(bits):
+            pos = bits * j + i
+            bit = (int(words[o, pos // 32]) >> (pos % 32)) & 1
+            assert bit == (int(q[o, j]) >> i) & 1
+
+
+def _levels_argmin(v, delta, zero, bits):
+    """Brute force: the code whose dequantized level is nearest to v (fp64)."""
+    lv = (np.arange(2 ** bits, dtype=np.float64)[None, :] - zero) * delta
+    return np.argmin(np.abs(v[:, None] - lv), axis=1)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 16), (4, 32), (5, 64), (4, 128), (3, 64)])
+def test_rtn_is_nearest_level_brute_force(bits, group):
+    rng = np.random.default_rng(100 * bits + group)
+    M, K = 12, 256
+    v = (rng.standard_normal((M, K)) * rng.lognormal(0, 1, size=(M, 1)) * 0.02).astype(np.float32)
+    v[0, :group] = np.abs(v[0, :group])          # an all-positive group
+    v[1, :group] = -np.abs(v[1, :group])         # an all-negative group
+    r = oracle.group_rtn(v, bits, group)
+    band = oracle.boundary_band(r["u"])
+    d = np.repeat(r["delta"].astype(np.float64), group, axis=1)
+    z = np.repeat(r["zero"].astype(np.float64), group, axis=1)
+    for o in range(M):
+        best = _levels_argmin(v[o].astype(np.float64), d[o][:, None], z[o][:, None], bits)
+        ok = ~band[o]
+        np.testing.assert_array_equal(r["q"][o][ok], best[ok])
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 16), (4, 32), (5, 128)])
+def test_rtn_invariants(bits, group):
+    rng = np.random.default_rng(7 * bits + group)
+    M, K = 16, 512
+    v = (rng.standard_t(3, size=(M, K)) * 0.05).astype(np.float32)
+    r = oracle.group_rtn(v, bits, group)
+    qmax = 2 ** bits - 1
+    q, dl, zz = r["q"], r["delta"].astype(np.float64), r["zero"].astype(np.float64)
+    assert q.min() >= 0 and q.max() <= qmax
+    assert zz.min() >= 0 and zz.max() <= qmax and np.all(zz == np.round(zz))
+    vg = v.astype(np.float64).reshape(M, K // group, group)
+    mn = np.minimum(0, vg.min(axis=2))
+    mx = np.maximum(0, vg.max(axis=2))
+    assert np.all(dl * qmax >= mx - mn)                 # grid covers the range
+    w_hat = oracle.dequant(q, r["delta"], r["zero"], group)
+    err = np.abs(w_hat - v).reshape(M, K // group, group)
+    assert np.all(err <= dl[:, :, None] / 2 * (1 + 1e-6))  # half a step at most
+    # 0 is exactly representable (integer zero point)
+    assert np.all((0 - zz) * dl <= 0) and np.all((qmax - zz) * dl >= 0)
+
+
+def test_rtn_power_of_two_scaling_invariance():
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal((8, 128)) * 0.03).astype(np.float32)
+    r1 = oracle.group_rtn(v, 4, 32)
+    for k in (-3, 2, 5):
+        r2 = oracle.group_rtn(v * np.float32(2.0 ** k), 4, 32)
+        np.testing.assert_array_equal(r2["q"], r1["q"])
+        np.testing.assert_array_equal(r2["zero"], r1["zero"])
+        np.testing.assert_array_equal(r2["delta"].astype(np.float64),
+                                      r1["delta"].astype(np.float64) * 2.0 ** k)
+
+
+def test_rtn_given_step_matches_torch_affine_quantizer():
+    # Given the step and zero point, the codes are the textbook affine
+    # quantizer round(v / delta) + z, clamped: compare with torch's own.
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    bits, group = 4, 32
+    v = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    r = oracle.group_rtn(v, bits, group)
+    vg = torch.from_numpy(v.reshape(-1, group))
+    scale = torch.from_numpy(r["delta"].astype(np.float64).reshape(-1))
+    zp = torch.from_numpy(r["zero"].astype(np.int64).reshape(-1))
+    tq = torch.quantize_per_channel(vg, scale, zp, 0, torch.quint8).int_repr().numpy()
+    tq = np.clip(tq.astype(np.int64), 0, 2 ** bits - 1).reshape(v.shape)
+    ok = ~oracle.boundary_band(r["u"])
+    np.testing.assert_array_equal(r["q"][ok], tq[ok])
+
+
+def test_rtn_step_and_zero_match_torch_minmax_observer():
+    # When (max - min)/(2^b - 1) is exactly an fp16 number, rounding it up
+    # changes nothing and the step/zero equal torch's asymmetric min/max
+    # observer (which also extends the range to contain 0).
+    torch = pytest.importorskip("torch")
+    from torch.ao.quantization.observer import MinMaxObserver
+    cases = [([-0.5, 0.25, 1.375, 0.0], 4), ([0.25, 0.5, 3.75, 1.0], 4),
+             ([-3.0, -1.0, -0.5, -2.0], 2), ([-0.375, 0.5, 0.25, 0.125], 3)]
+    for vals, bits in cases:
+        v = np.array([vals], dtype=np.float32)
+        r = oracle.group_rtn(v, bits, 4)
+        obs = MinMaxObserver(dtype=torch.quint8, qscheme=torch.per_tensor_affine,
+                             quant_min=0, quant_max=2 ** bits - 1)
+        obs(torch.from_numpy(v))
+        sc, zp = obs.calculate_qparams()
+        assert float(r["delta"][0, 0]) == float(sc)
+        assert int(r["zero"][0, 0]) == int(zp)
+
+
+def test_rtn_degenerate_groups():
+    v = np.zeros((2, 32), dtype=np.float32)
+    v[1, :16] = np.nan
+    v[1, 16:] = np.linspace(-1, 1, 16, dtype=np.float32)
+    r = oracle.group_rtn(v, 4, 16)
+    # constant-zero group: step 1, zero 0, codes 0, dequantizes to exact 0
+    assert float(r["delta"][0, 0]) == 1.0 and float(r["zero"][0, 0]) == 0.0
+    assert not r["q"][0].any()
+    # an all-NaN group: min/max ignore NaN -> the zero-group rule; NaN -> code 0
+    assert float(r["delta"][1, 0]) == 1.0 and not r["q"][1, :16].any()
+    assert float(r["zero"][1, 1]) == 7.0  # rne(1 / fp16up(2/15)) = rne(7.498)
+
+
+def test_alpha_zero_reduces_to_plain_rtn_of_w():
+    # [TTQ §results] baselines: with alpha = 0 the method is plain group RTN
+    wl = synth.workload("c1", T=32, K=256, M=64)
+    d = synth.make_inputs(wl)
+    out = oracle.linear(d["X"], "f32", d["W"], "f32", 4, 32, 0.0, 1e-2)
+    np.testing.assert_array_equal(out["s"], np.ones(256, np.float32))
+    np.testing.assert_array_equal(out["v"], d["W"])
+    r = oracle.group_rtn(d["W"], 4, 32)
+    np.testing.assert_array_equal(out["q"], r["q"])
+
+
+# ------------------------------------------------------------- projection
+
+def test_projection_brute_force_loops():
+    rng = np.random.default_rng(8)
+    T, K, M = 3, 32, 4
+    X = synth.encode(rng.standard_normal((T, K)), "bf16")
+    s = (rng.random(K) + 0.5).astype(np.float32)
+    W = synth.encode(rng.standard_normal((M, K)) * 0.1, "f32")
+    v = oracle.quant_values(W, "f32", s)
+    r = oracle.group_rtn(v, 3, 16)
+    w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], 16)
+    Y = oracle.project(X, "bf16", s, w_hat)
+    xf = synth.bf16_bits_to_f32(X)
+    for t in range(T):
+        for o in range(M):
+            acc = 0.0
+            for j in range(K):
+                G = j // 16
+                wq = (int(r["q"][o, j]) - float(r["zero"][o, G])) * float(r["delta"][o, G])
+                acc += wq * (float(xf[t, j]) / float(s[j]))
+            assert Y[t, o] == pytest.approx(acc, rel=1e-12, abs=1e-14)
+
+
+def test_projection_identity_input_exposes_layout():
+    # X = I (T = K): row t of Y is column t of the effective weight, i.e.
+    # Y[t][o] = w_hat[o][t] / s[t].  Any transposition or packing error shows.
+    rng = np.random.default_rng(9)
+    K, M = 64, 48
+    X = synth.encode(np.eye(K), "bf16")
+    s = (rng.random(K) + 0.5).astype(np.float32)
+    W = synth.encode(rng.standard_normal((M, K)) * 0.05, "bf16")
+    r = oracle.group_rtn(oracle.quant_values(W, "bf16", s), 4, 32)
+    q2 = oracle.unpack_codes(oracle.pack_codes(r["q"], 4), 4, K)
+    w_hat = oracle.dequant(q2, r["delta"], r["zero"], 32)
+    Y = oracle.project(X, "bf16", s, w_hat)
+    np.testing.assert_allclose(Y, (w_hat / s.astype(np.float64)[None, :]).T, rtol=1e-15, atol=0)
+
+
+def test_output_error_within_half_step_bound():
+    # |Y - X W^T| <= sum_j |x_tj| delta_oj / (2 s_j): a bound from the
+    # half-step property alone ([TTQ §method b1] RTN; b2 scaling).
+    wl = synth.workload("c2", T=16, K=256, M=40)
+    d = synth.make_inputs(wl)
+    out = oracle.linear(d["X"], "bf16", d["W"], "bf16", 4, 32, 0.5, 1e-2)
+    x = synth.bf16_bits_to_f32(d["X"]).astype(np.float64)
+    w = synth.bf16_bits_to_f32(d["W"]).astype(np.float64)
+    s = out["s"].astype(np.float64)
+    exact = x @ w.T
+    # v = fp32(W s) adds at most half an fp32 ulp of v per element
+    dlt = np.repeat(out["delta"].astype(np.float64), 32, axis=1)
+    per = (dlt / 2 + np.abs(w * s) * 2.0 ** -24) / s[None, :]
+    bound = np.abs(x) @ per.T
+    assert np.all(np.abs(out["Y"] - exact) <= bound * (1 + 1e-9))
+
+
+def test_activation_aware_loss_not_above_rtn_on_outlier_inputs():
+    # [TTQ §method b3] objective L = ||(W - W_hat) X||^2; with outlier
+    # channels the AWQ-scaled quantization must not lose to plain RTN.
+    wl = synth.workload("c1")
+    d = synth.make_inputs(wl)
+    res = {}
+    for alpha in (0.0, 0.5):
+        out = oracle.linear(d["X"], "f32", d["W"], "f32", 4, 32, alpha, 1e-2)
+        w_eff = oracle.effective_weight(out["w_hat"], out["s"])
+        res[alpha] = oracle.loss(d["X"], "f32", d["W"], "f32", w_eff)
+    assert res[0.5] <= res[0.0]
+    assert res[0.5] / res[0.0] < 0.8  # by a wide margin on x20 outliers
+
+
+# --------------------------------------------------------------- low rank
+
+def _jacobi_eigenvalues(S, sweeps=60):
+    """Cyclic Jacobi eigenvalue iteration for a small symmetric matrix
+    (pure Python lists; independent of LAPACK)."""
+    n = len(S)
+    a = [row[:] for row in S]
+    for _ in range(sweeps):
+        off = sum(a[i][j] ** 2 for i in range(n) for j in range(n) if i != j)
+        if off < 1e-30:
+            break
+        for p in range(n - 1):
+            for q in range(p + 1, n):
+                if abs(a[p][q]) < 1e-300:
+                    continue
+                theta = (a[q][q] - a[p][p]) / (2 * a[p][q])
+                t = math.copysign(1.0, theta) / (abs(theta) + math.sqrt(theta * theta + 1))
+                c = 1 / math.sqrt(t * t + 1)
+                s = t * c
+                for k in range(n):
+                    akp, akq = a[k][p], a[k][q]
+                    a[k][p] = c * akp - s * akq
+                    a[k][q] = s * akp + c * akq
+                for k in range(n):
+                    apk, aqk = a[p][k], a[q][k]
+                    a[p][k] = c * apk - s * aqk
+                    a[q][k] = s * apk + c * aqk
+    return sorted((a[i][i] for i in range(n)), reverse=True)
+
+
+def test_lowrank_eight_by_eight_brute_force():
+    rng = np.random.default_rng(11)
+    K = M = 8
+    W = synth.encode(rng.standard_normal((M, K)), "f32")
+    X = synth.encode(rng.standard_normal((5, K)) * 2, "f32")
+    s = (rng.random(K) + 0.5).astype(np.float32)
+    ws = W.astype(np.float64) * s.astype(np.float64)[None, :]
+    G = (ws.T @ ws).tolist()
+    sig2 = _jacobi_eigenvalues(G)
+    for r in range(1, 8):
+        B, A = oracle.lowrank_factors(W, "f32", s, r)
+        resid = (W.astype(np.float64) - B.astype(np.float64) @ A.astype(np.float64)) * s[None, :]
+        # Eckart-Young: the best rank-r residual energy is the tail of sigma^2
+        assert np.sum(resid ** 2) == pytest.approx(sum(sig2[r:]), rel=1e-5, abs=1e-9)
+    # the pipeline's output equals the dense triple sum, element by element
+    r = 3
+    B, A = oracle.lowrank_factors(W, "f32", s, r)
+    v = oracle.quant_values(W, "f32", s, B, A)
+    q = oracle.group_rtn(v, 5, 8)
+    w_hat = oracle.dequant(q["q"], q["delta"], q["zero"], 8)
+    Y = oracle.project(X, "f32", s, w_hat, B, A)
+    for t in range(5):
+        for o in range(M):
+            acc = 0.0
+            for j in range(K):
+                acc += w_hat[o, j] / float(s[j]) * float(X[t, j])
+                for k in range(r):
+                    acc += float(B[o, k]) * float(A[k, j]) * float(X[t, j])
+            assert Y[t, o] == pytest.approx(acc, rel=1e-12, abs=1e-12)
+
+
+def test_lowrank_residual_sign_and_scale():
+    # [TTQ §method b5] W = W_q + B A: the effective weight (quantized
+    # residual + B A) must stay within half a step of W, element-wise.
+    wl = synth.workload("c5", T=8, K=128, M=64)
+    d = synth.make_inputs(wl)
+    X, W = d["X"], d["W"]
+    out0 = oracle.linear(X, "bf16", W, "bf16", 2, 32, 0.5, 1e-2)
+    B, A = oracle.lowrank_factors(W, "bf16", out0["s"], 16)
+    out = oracle.linear(X, "bf16", W, "bf16", 2, 32, 0.5, 1e-2, B=B, A=A)
+    w_eff = oracle.effective_weight(out["w_hat"], out["s"], B, A)
+    w = oracle.decode(W, "bf16")
+    s = out["s"].astype(np.float64)
+    dl = np.repeat(out["delta"].astype(np.float64), 32, axis=1)
+    slack = 1e-5 * (np.abs(w) + np.abs(B.astype(np.float64) @ A.astype(np.float64)))
+    assert np.all(np.abs(w_eff - w) <= dl / (2 * s[None, :]) + slack)
+    # and with the planted rank-16 part removed, the residual steps shrink
+    assert np.median(out["delta"].astype(np.float64)) < np.median(out0["delta"].astype(np.float64))
