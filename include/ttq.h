@@ -1,0 +1,192 @@
+/*
+ * libttq — activation-aware test-time quantization (TTQ) of one linear layer,
+ * per prompt, on AMD MI355X (gfx950).
+ *
+ * Source of the method: the nubint.ai review page "TTQ: Activation-Aware
+ * Test-Time Quantization to Accelerate LLM Inference On The Fly", section
+ * "proposed method" (bullets b1..b7).  "[TTQ §method b3]" below means its
+ * third bullet.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Shapes: T tokens, K input channels, M output channels.
+ *    X is [T][K] row-major with row stride ldx (elements),
+ *    W is [M][K] row-major with row stride ldw (the Linear weight layout),
+ *    Y is [T][M] row-major with row stride ldy.
+ *  - Every pointer is DEVICE memory, allocated and owned by the caller; the
+ *    library allocates nothing, keeps no global mutable state and never
+ *    synchronises.  Every call only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL = the null stream) and returns; results are ready
+ *    when the stream reaches that point.
+ *  - Packed codes: for each output row, the K codes form a little-endian bit
+ *    stream (code j occupies stream bits [bits*j, bits*j + bits), least
+ *    significant bit first; stream bit i is bit i%32 of int32 word i/32).
+ *    codes is dense: [M][K*bits/32] int32.
+ *  - Per-group step and zero point: fp16 bit patterns, dense [M][K/group];
+ *    the group of channel j is j / group (consecutive input channels of one
+ *    output row).  The zero point is an integer stored as fp16.
+ *  - Argument checks run on the host before any HIP call.  A failed check
+ *    returns TTQ_ERR_INVALID (or TTQ_ERR_UNSUPPORTED for well-formed but
+ *    unimplemented options) and launches nothing.  A failed launch returns
+ *    TTQ_ERR_DEVICE.  Faults during execution surface at the caller's next
+ *    synchronisation.  After a non-OK status the outputs are undefined.
+ *    ttq_last_error() describes the last non-OK status of the calling thread.
+ *  - Alignment: X, W and codes base pointers 16-byte aligned and the X/W row
+ *    strides a multiple of 16 bytes; Y aligned to its element size, any row
+ *    stride >= M; s 16-byte aligned; ssq 8-byte aligned; workspace 256-byte
+ *    aligned.
+ *  - Limits: K a positive multiple of 32 (of 8 for ttq_stats); bits in
+ *    {2,3,4,5}; group in {16,32,64,128} dividing K; 0 <= rank <= 32.
+ *    T == 0 or M == 0 is a valid empty call (nothing is launched, except
+ *    that ttq_stats with accumulate == 0 still zeroes ssq).
+ *  - Inputs are expected to be finite.  Non-finite inputs give unspecified
+ *    (but memory-safe) outputs.
+ */
+#ifndef TTQ_H
+#define TTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TTQ_OK = 0,
+    TTQ_ERR_INVALID = 1,      /* malformed arguments: nothing launched      */
+    TTQ_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (p != 2)   */
+    TTQ_ERR_DEVICE = 3        /* the HIP runtime refused a launch           */
+} ttq_status;
+
+typedef enum {
+    TTQ_F32 = 0,              /* IEEE binary32                              */
+    TTQ_BF16 = 1              /* bfloat16 (upper half of a binary32)        */
+} ttq_dtype;
+
+/*
+ * ttq_stats — per-channel sum of squares of the prompt's activations.
+ * [TTQ §method b2, b3]: the diagonal of the input covariance, estimated
+ * online from the prompt itself.
+ *   ssq[j] (+)= sum_{t<T} X[t][j]^2, accumulated in fp64.
+ *   X: [T][K] fp32 or bf16 (xt), stride ldx >= K.   ssq: [K] fp64, output.
+ *   accumulate != 0 adds to the existing ssq (chunked prefill), else
+ *   overwrites it.  ws: scratch of at least ttq_workspace_bytes(T,K,0,...)
+ *   bytes (partial sums; fixed reduction order, so results are bitwise
+ *   reproducible run to run).  K must be a multiple of 8.
+ */
+ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
+                     double* ssq, int accumulate, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * ttq_awq_scales — shrunk AWQ per-channel scales.
+ * [TTQ §method b2-b4]: c = ssq / n_tokens; lambda = lambda_rel * mean(c)
+ * (shrinkage C + lambda I); s[j] = (c[j] + lambda)^(alpha / p), evaluated in
+ * fp64 and rounded once to fp32; s[j] = 1 where c[j] + lambda == 0.
+ * alpha, lambda_rel, p are fixed in advance (no search).
+ *   ssq: [K] fp64 input.  s: [K] fp32 output.  n_tokens > 0.
+ *   alpha and lambda_rel finite and >= 0.  p must be 2 (second moment), any
+ *   other value returns TTQ_ERR_UNSUPPORTED.
+ */
+ttq_status ttq_awq_scales(const double* ssq, int64_t n_tokens, int64_t K,
+                          float alpha, float lambda_rel, float p, float* s,
+                          void* stream);
+
+/*
+ * ttq_quantize_groups — group-wise RTN of the scaled (residual) weight.
+ * [TTQ §method b1] group-wise RTN; [TTQ §method b2] the weight is scaled by
+ * s per input channel; [TTQ §method b5] with low-rank factors the residual
+ * W - B A is quantized.
+ *   v[o][j] = fp32( (W[o][j] - sum_{k<rank} B[o][k] A[k][j]) * s[j] ), the
+ *     residual accumulated in fp64 in rank order; without factors this is
+ *     the correctly rounded fp32 product W*s.
+ *   Per group: mn = min(0, min v), mx = max(0, max v);
+ *     step = fp16 rounded up of fp32(mx - mn) / (2^bits - 1) (1 if zero);
+ *     zero = clamp(rne(-mn / step), 0, 2^bits - 1);
+ *     code = clamp(rne(v / step) + zero, 0, 2^bits - 1).
+ *   W: [M][K] fp32/bf16 (wt), stride ldw.  s: [K] fp32, or NULL for s = 1.
+ *   B: [M][rank] fp32 dense, A: [rank][K] fp32 dense; both NULL iff rank 0.
+ *   Outputs: codes [M][K*bits/32], scale_f16 and zero_f16 [M][K/group].
+ *   Codes whose v/step lies within ~1e-5 of a step of a rounding boundary
+ *   may differ from an exact-division evaluation (v * (1/step) is used).
+ */
+ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int64_t ldw,
+                               const float* s, int bits, int group,
+                               const float* B, const float* A, int rank,
+                               int32_t* codes, uint16_t* scale_f16, uint16_t* zero_f16,
+                               void* stream);
+
+/*
+ * ttq_qgemm — the quantized projection Y = W_hat (X / s).
+ * [TTQ §method b7] quantized projection kernel; [TTQ §method b1] QDQ:
+ * W_hat[o][j] = (code - zero) * step; [TTQ §method b2] inputs divided by s.
+ *   Y[t][o] = sum_j W_hat[o][j] * X[t][j] / s[j].
+ *   The dequantized weight (code - zero) * step / s[j] is rounded once to
+ *   bf16 and multiplied with X on the matrix cores with fp32 accumulation
+ *   (bf16 X is used as is; fp32 X is split into two bf16 halves and the
+ *   weight too, three products, for near-fp32 accuracy).
+ *   X: [T][K] (xt), s: [K], codes/scale/zero as produced by
+ *   ttq_quantize_groups for (M, K, bits, group).  Y: [T][M] fp32 or bf16
+ *   (yt), overwritten.  Y must not overlap any input.
+ *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes.
+ */
+ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
+                     const float* s, const int32_t* codes, const uint16_t* scale_f16,
+                     const uint16_t* zero_f16, int64_t M, int bits, int group,
+                     void* Y, int yt, int64_t ldy, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * ttq_lowrank_add — Y += B (A X), the dynamic low-rank term.
+ * [TTQ §method b5]: W = W_q + B A, so the layer adds B (A X) to the
+ * quantized projection.  Computed in fp32: Z[t][k] = sum_j A[k][j] X[t][j],
+ * then Y[t][o] += sum_k B[o][k] Z[t][k].
+ *   X: [T][K] (xt), A: [rank][K] fp32, B: [M][rank] fp32, Y: [T][M] (yt),
+ *   updated in place.  ws: at least ttq_workspace_bytes(T, K, M, 2, 32, rank).
+ */
+ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
+                           const float* A, const float* B, int64_t M, int rank,
+                           void* Y, int yt, int64_t ldy, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Workspace size (bytes) sufficient for every call above and for ttq_linear
+ * with these sizes (including the intermediate ssq, s, codes, steps and
+ * zeros that ttq_linear keeps there when the caller does not supply them).
+ * Returns 0 for arguments that no call accepts.
+ */
+size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group, int rank);
+
+/*
+ * ttq_linear — the whole per-prompt path of one linear layer.
+ * [TTQ §method b1-b5, b7]: statistics of this prompt's X -> shrunk AWQ
+ * scales -> group RTN of (W - B A) diag(s) -> quantized projection, plus
+ * B (A X) when rank > 0.  Equivalent to the five calls above in order.
+ * The optional outputs (ssq, s, codes, scale_f16, zero_f16) receive the
+ * prompt's quantization state so that later decode steps can call ttq_qgemm
+ * on it; when NULL they live in the workspace.
+ */
+typedef struct ttq_linear_args {
+    const void* X;  int xt;  int64_t T;  int64_t K;  int64_t ldx;
+    const void* W;  int wt;  int64_t M;  int64_t ldw;
+    float alpha;  float lambda_rel;  float p;
+    int bits;  int group;
+    const float* B;  const float* A;  int rank;
+    void* Y;  int yt;  int64_t ldy;
+    double* ssq;  float* s;  int32_t* codes;  uint16_t* scale_f16;  uint16_t* zero_f16;
+} ttq_linear_args;
+
+ttq_status ttq_linear(const ttq_linear_args* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* ttq_status_str(int status);
+
+/* Text describing the calling thread's last non-OK status ("" if none). */
+const char* ttq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTQ_H */

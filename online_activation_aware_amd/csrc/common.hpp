@@ -1,0 +1,61 @@
+// Device helpers shared by the libttq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttq {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t packed) {
+    return __builtin_bit_cast(float, packed << 16);
+}
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t packed) {
+    return __builtin_bit_cast(float, packed & 0xFFFF0000u);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
+}
+// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// fp16 bit pattern <-> fp32.
+__device__ __forceinline__ float f16_to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// fp32 -> fp16 rounded toward +infinity, for x >= 0 (NaN-free).
+__device__ __forceinline__ uint16_t f32_to_f16_up(float x) {
+    uint16_t h = f32_to_f16_rne(x);
+    if (f16_to_f32(h) < x) h = (uint16_t)(h + 1);   // next fp16 up (x >= 0)
+    return h;
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_nc(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+}  // namespace ttq

@@ -1,0 +1,144 @@
+// Dynamic low-rank term Y += B (A X), fp32.
+//
+// [TTQ §method b5]: W = W_q + B A, so the quantized layer adds B (A X).
+// The term is kept in fp32 end to end: it can carry much of Y's energy.
+//
+// k_lowrank_z: one wave per 64 tokens and K slice (lane = token); A's values
+// are the same for every lane, so they come through scalar loads, and each
+// lane accumulates rank partial sums of its token over the slice.
+// k_lowrank_y: a 64 x 64 (tokens x rows) tile per workgroup; the slice
+// partials are summed in slice order into LDS together with the B rows, and
+// each thread adds a 4 x 4 block of B Z^T into Y.  No atomics.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ttq {
+
+constexpr int kMaxRank = 32;
+
+template <bool XF32, int RMAX>
+__global__ __launch_bounds__(64) void k_lowrank_z(const void* __restrict__ X, int64_t T, int64_t K,
+                                                  int64_t ldx, const float* __restrict__ A, int rank,
+                                                  int64_t slice, float* __restrict__ Zp) {
+    const int lane = threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t j0 = (int64_t)blockIdx.y * slice;
+    const int64_t j1 = min(K, j0 + slice);
+    float z[RMAX];
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k) z[k] = 0.f;
+    if (t < T) {
+        for (int64_t j = j0; j < j1; j += 8) {
+            float x[8];
+            if constexpr (XF32) {
+                const f32x4* p = (const f32x4*)((const float*)X + t * ldx + j);
+                f32x4 a = ld_nc(p), b = ld_nc(p + 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+            } else {
+                u32x4 w = ld_nc((const u32x4*)((const uint16_t*)X + t * ldx + j));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo_to_f32(w[i]); x[2 * i + 1] = bf16hi_to_f32(w[i]); }
+            }
+#pragma unroll
+            for (int k = 0; k < RMAX; ++k) {
+                if (k >= rank) break;
+                const float* ak = A + (int64_t)k * K + j;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) z[k] = __builtin_fmaf(ak[i], x[i], z[k]);
+            }
+        }
+        float* zo = Zp + ((int64_t)blockIdx.y * T + t) * rank;
+#pragma unroll
+        for (int k = 0; k < RMAX; ++k)
+            if (k < rank) zo[k] = z[k];
+    }
+}
+
+template <bool YF32, int RMAX>
+__global__ __launch_bounds__(256) void k_lowrank_y(const float* __restrict__ Zp, int nslices,
+                                                   const float* __restrict__ B, int rank, int64_t T,
+                                                   int64_t M, void* __restrict__ Y, int64_t ldy) {
+    __shared__ float sZ[64][RMAX + 1];
+    __shared__ float sB[64][RMAX + 1];
+    const int tid = threadIdx.x;
+    const int64_t tb = (int64_t)blockIdx.y * 64, ob = (int64_t)blockIdx.x * 64;
+    for (int idx = tid; idx < 64 * RMAX; idx += 256) {
+        const int r = idx / RMAX, k = idx % RMAX;
+        float zs = 0.f, bv = 0.f;
+        if (k < rank) {
+            if (tb + r < T)
+                for (int sl = 0; sl < nslices; ++sl) zs += Zp[((int64_t)sl * T + tb + r) * rank + k];
+            if (ob + r < M) bv = B[(ob + r) * rank + k];
+        }
+        sZ[r][k] = zs;
+        sB[r][k] = bv;
+    }
+    __syncthreads();
+    const int tt = (tid >> 4) * 4, oo = (tid & 15) * 4;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < RMAX; ++k)
+                if (k < rank) s = __builtin_fmaf(sB[oo + b][k], sZ[tt + a][k], s);
+            acc[a][b] = s;
+        }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int64_t t = tb + tt + a;
+        if (t >= T) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t o = ob + oo + b;
+            if (o >= M) continue;
+            if constexpr (YF32) {
+                float* yp = (float*)Y + t * ldy + o;
+                *yp = *yp + acc[a][b];
+            } else {
+                uint16_t* yp = (uint16_t*)Y + t * ldy + o;
+                *yp = (uint16_t)f32_to_bf16(bf16_to_f32(*yp) + acc[a][b]);
+            }
+        }
+    }
+}
+
+int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len) {
+    const int64_t tblocks = (T + 63) / 64;
+    int64_t ns = tblocks >= 512 ? 1 : (512 + tblocks - 1) / tblocks;
+    int64_t len = (K + ns - 1) / ns;
+    len = (len + 7) / 8 * 8;
+    if (len < 64) len = 64;
+    *slice_len = len;
+    return (int)((K + len - 1) / len);
+}
+
+template <int RMAX>
+static hipError_t launch_lr(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
+                            const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
+                            int64_t ldy, float* Zp, hipStream_t st) {
+    int64_t len = 0;
+    const int ns = lowrank_slices(T, K, &len);
+    dim3 gz((unsigned)((T + 63) / 64), (unsigned)ns);
+    if (xf32) k_lowrank_z<true, RMAX><<<gz, 64, 0, st>>>(X, T, K, ldx, A, rank, len, Zp);
+    else k_lowrank_z<false, RMAX><<<gz, 64, 0, st>>>(X, T, K, ldx, A, rank, len, Zp);
+    dim3 gy((unsigned)((M + 63) / 64), (unsigned)((T + 63) / 64));
+    if (yf32) k_lowrank_y<true, RMAX><<<gy, 256, 0, st>>>(Zp, ns, B, rank, T, M, Y, ldy);
+    else k_lowrank_y<false, RMAX><<<gy, 256, 0, st>>>(Zp, ns, B, rank, T, M, Y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
+                          const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
+                          int64_t ldy, float* Zp, hipStream_t st) {
+    // The accumulators are sized by the smallest of 8/16/32 that holds rank.
+    if (rank <= 8) return launch_lr<8>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
+    if (rank <= 16) return launch_lr<16>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
+    if (rank <= kMaxRank) return launch_lr<32>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ttq

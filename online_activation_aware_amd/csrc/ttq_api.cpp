@@ -1,0 +1,311 @@
+// The libttq C ABI: argument validation, workspace layout, launches.
+//
+// Every check runs on the host before any HIP call; a failed check returns
+// TTQ_ERR_INVALID / TTQ_ERR_UNSUPPORTED and launches nothing.  The library
+// keeps no global mutable state other than the per-thread error text.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ttq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ttq_status fail(ttq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ttq_status fail(ttq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+ttq_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return TTQ_OK;
+    return fail(TTQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int kMaxRank = 32;
+constexpr size_t kAlign = 256;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+bool dtype_ok(int t) { return t == TTQ_F32 || t == TTQ_BF16; }
+size_t esize(int t) { return t == TTQ_F32 ? 4 : 2; }
+bool bits_ok(int b) { return b >= 2 && b <= 5; }
+bool group_ok(int g) { return g == 16 || g == 32 || g == 64 || g == 128; }
+bool dim_ok(int64_t n) { return n >= 0 && n <= kMaxDim; }
+
+#define TTQ_REQUIRE(cond, ...)                                \
+    do {                                                      \
+        if (!(cond)) return fail(TTQ_ERR_INVALID, __VA_ARGS__); \
+    } while (0)
+
+// Checks for the output Y [T][M]: element-aligned, any row stride >= M.
+ttq_status check_output(const void* p, int t, int64_t rows, int64_t M, int64_t ld) {
+    TTQ_REQUIRE(dtype_ok(t), "Y: unknown dtype %d", t);
+    TTQ_REQUIRE(ld >= M && ld <= kMaxDim, "Y: row stride %lld < row length %lld", (long long)ld, (long long)M);
+    if (rows > 0 && M > 0) {
+        TTQ_REQUIRE(p != nullptr, "Y: null pointer");
+        TTQ_REQUIRE(aligned(p, esize(t)), "Y: pointer not aligned to its element size");
+    }
+    return TTQ_OK;
+}
+
+// Checks for a [rows][K] row-major matrix argument of dtype t.
+ttq_status check_matrix(const char* name, const void* p, int t, int64_t rows, int64_t K, int64_t ld) {
+    TTQ_REQUIRE(dtype_ok(t), "%s: unknown dtype %d", name, t);
+    TTQ_REQUIRE(ld >= K && ld <= kMaxDim, "%s: row stride %lld < row length %lld", name, (long long)ld, (long long)K);
+    if (rows > 0) {
+        TTQ_REQUIRE(p != nullptr, "%s: null pointer", name);
+        TTQ_REQUIRE(aligned(p, 16), "%s: pointer not 16-byte aligned", name);
+        TTQ_REQUIRE((ld * (int64_t)esize(t)) % 16 == 0, "%s: row stride is not a multiple of 16 bytes", name);
+    }
+    return TTQ_OK;
+}
+
+ttq_status check_quant_shape(int64_t M, int64_t K, int bits, int group) {
+    TTQ_REQUIRE(dim_ok(M), "M out of range");
+    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 32 == 0, "K must be a positive multiple of 32");
+    if (!bits_ok(bits)) return fail(TTQ_ERR_INVALID, "bits must be 2, 3, 4 or 5 (got %d)", bits);
+    if (!group_ok(group)) return fail(TTQ_ERR_INVALID, "group must be 16, 32, 64 or 128 (got %d)", group);
+    TTQ_REQUIRE(K % group == 0, "K must be a multiple of the group size");
+    return TTQ_OK;
+}
+
+ttq_status check_state(const float* s, const void* codes, const void* scale, const void* zero, bool need_s) {
+    TTQ_REQUIRE(!need_s || s != nullptr, "s: null pointer");
+    TTQ_REQUIRE(s == nullptr || aligned(s, 16), "s: pointer not 16-byte aligned");
+    TTQ_REQUIRE(codes != nullptr && aligned(codes, 16), "codes: null or not 16-byte aligned");
+    TTQ_REQUIRE(scale != nullptr && aligned(scale, 2), "scale_f16: null or misaligned");
+    TTQ_REQUIRE(zero != nullptr && aligned(zero, 2), "zero_f16: null or misaligned");
+    return TTQ_OK;
+}
+
+ttq_status check_lowrank(const float* B, const float* A, int rank, bool allow_zero) {
+    TTQ_REQUIRE(rank >= (allow_zero ? 0 : 1) && rank <= kMaxRank, "rank must be in [%d, %d] (got %d)",
+                allow_zero ? 0 : 1, kMaxRank, rank);
+    TTQ_REQUIRE((B == nullptr) == (rank == 0) && (A == nullptr) == (rank == 0),
+                "B and A must both be given iff rank > 0");
+    TTQ_REQUIRE(B == nullptr || (aligned(B, 4) && aligned(A, 4)), "B/A: misaligned");
+    return TTQ_OK;
+}
+
+ttq_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return TTQ_OK;
+    TTQ_REQUIRE(ws != nullptr, "workspace: null pointer (%zu bytes needed)", need);
+    TTQ_REQUIRE(aligned(ws, kAlign), "workspace: pointer not 256-byte aligned");
+    TTQ_REQUIRE(ws_bytes >= need, "workspace: %zu bytes given, %zu needed", ws_bytes, need);
+    return TTQ_OK;
+}
+
+size_t ws_stats(int64_t T, int64_t K) {
+    int rows = 0;
+    const int nch = ttq::stats_chunks(T, K, &rows);
+    return round_up((size_t)nch * (size_t)K * sizeof(double));
+}
+size_t ws_qgemm(int64_t K) { return round_up((size_t)K * sizeof(float)); }
+size_t ws_lowrank(int64_t T, int64_t K, int rank) {
+    if (rank <= 0 || T <= 0) return 0;
+    int64_t len = 0;
+    const int ns = ttq::lowrank_slices(T, K, &len);
+    return round_up((size_t)ns * (size_t)T * (size_t)rank * sizeof(float));
+}
+
+struct StateLayout {
+    size_t ssq, s, codes, scale, zero, scratch, total;
+};
+StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, int rank) {
+    StateLayout L{};
+    size_t off = 0;
+    L.ssq = off;     off += round_up((size_t)K * sizeof(double));
+    L.s = off;       off += round_up((size_t)K * sizeof(float));
+    L.codes = off;   off += round_up((size_t)M * (size_t)(K * bits / 32) * sizeof(int32_t));
+    L.scale = off;   off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
+    L.zero = off;    off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
+    L.scratch = off;
+    size_t scratch = ws_stats(T, K);
+    if (ws_qgemm(K) > scratch) scratch = ws_qgemm(K);
+    if (ws_lowrank(T, K, rank) > scratch) scratch = ws_lowrank(T, K, rank);
+    L.total = off + scratch;
+    return L;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ttq_status_str(int status) {
+    switch (status) {
+        case TTQ_OK: return "TTQ_OK";
+        case TTQ_ERR_INVALID: return "TTQ_ERR_INVALID";
+        case TTQ_ERR_UNSUPPORTED: return "TTQ_ERR_UNSUPPORTED";
+        case TTQ_ERR_DEVICE: return "TTQ_ERR_DEVICE";
+    }
+    return "TTQ_ERR_UNKNOWN";
+}
+
+const char* ttq_last_error(void) { return g_last_error.c_str(); }
+
+size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group, int rank) {
+    if (!dim_ok(T) || !dim_ok(M) || K <= 0 || K > kMaxDim || K % 32 || !bits_ok(bits) ||
+        !group_ok(group) || K % group || rank < 0 || rank > kMaxRank)
+        return 0;
+    return state_layout(T, K, M, bits, group, rank).total;
+}
+
+ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, double* ssq,
+                     int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(dim_ok(T), "T out of range");
+    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 8 == 0, "K must be a positive multiple of 8");
+    if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
+    TTQ_REQUIRE(ssq != nullptr && aligned(ssq, 8), "ssq: null or not 8-byte aligned");
+    const size_t need = T > 0 ? ws_stats(T, K) : 0;
+    if (ttq_status e = check_ws(ws, ws_bytes, need)) return e;
+    if (T == 0 && accumulate) return TTQ_OK;
+    return device_status(ttq::launch_stats(X, xt == TTQ_F32, T, K, ldx, ssq, accumulate,
+                                           (double*)ws, as_stream(stream)),
+                         "ttq_stats launch");
+}
+
+ttq_status ttq_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
+                          float lambda_rel, float p, float* s, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(K > 0 && K <= kMaxDim, "K out of range");
+    TTQ_REQUIRE(n_tokens > 0, "n_tokens must be positive");
+    TTQ_REQUIRE(ssq != nullptr && aligned(ssq, 8), "ssq: null or not 8-byte aligned");
+    TTQ_REQUIRE(s != nullptr && aligned(s, 16), "s: null or not 16-byte aligned");
+    TTQ_REQUIRE(std::isfinite(alpha) && alpha >= 0.f, "alpha must be finite and >= 0");
+    TTQ_REQUIRE(std::isfinite(lambda_rel) && lambda_rel >= 0.f, "lambda_rel must be finite and >= 0");
+    TTQ_REQUIRE(std::isfinite(p) && p > 0.f, "p must be finite and > 0");
+    if (p != 2.0f) return fail(TTQ_ERR_UNSUPPORTED, "only p = 2 (second-moment statistics) is implemented");
+    return device_status(ttq::launch_awq_scales(ssq, n_tokens, K, alpha, lambda_rel, s, as_stream(stream)),
+                         "ttq_awq_scales launch");
+}
+
+ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int64_t ldw,
+                               const float* s, int bits, int group, const float* B, const float* A,
+                               int rank, int32_t* codes, uint16_t* scale_f16, uint16_t* zero_f16,
+                               void* stream) {
+    g_last_error.clear();
+    if (ttq_status e = check_quant_shape(M, K, bits, group)) return e;
+    if (ttq_status e = check_matrix("W", W, wt, M, K, ldw)) return e;
+    if (ttq_status e = check_lowrank(B, A, rank, true)) return e;
+    if (M == 0) return TTQ_OK;
+    if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, false)) return e;
+    return device_status(ttq::launch_quantize(W, wt == TTQ_F32, M, K, ldw, s, bits, group, B, A, rank,
+                                              (uint32_t*)codes, scale_f16, zero_f16, as_stream(stream)),
+                         "ttq_quantize_groups launch");
+}
+
+ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, const float* s,
+                     const int32_t* codes, const uint16_t* scale_f16, const uint16_t* zero_f16,
+                     int64_t M, int bits, int group, void* Y, int yt, int64_t ldy, void* ws,
+                     size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(dim_ok(T), "T out of range");
+    if (ttq_status e = check_quant_shape(M, K, bits, group)) return e;
+    if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
+    if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
+    if (T == 0 || M == 0) return TTQ_OK;
+    if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
+    if (ttq_status e = check_ws(ws, ws_bytes, ws_qgemm(K))) return e;
+    float* inv = (float*)ws;
+    hipStream_t st = as_stream(stream);
+    if (ttq_status e = device_status(ttq::launch_inv_scales(s, K, inv, st), "ttq_qgemm launch")) return e;
+    return device_status(ttq::launch_qgemm(X, xt == TTQ_F32, T, K, ldx, inv, (const uint32_t*)codes,
+                                           scale_f16, zero_f16, M, bits, group, Y, yt == TTQ_F32, ldy, st),
+                         "ttq_qgemm launch");
+}
+
+ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, const float* A,
+                           const float* B, int64_t M, int rank, void* Y, int yt, int64_t ldy, void* ws,
+                           size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(dim_ok(T) && dim_ok(M), "T or M out of range");
+    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 8 == 0, "K must be a positive multiple of 8");
+    if (ttq_status e = check_lowrank(B, A, rank, false)) return e;
+    if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
+    if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
+    if (T == 0 || M == 0) return TTQ_OK;
+    if (ttq_status e = check_ws(ws, ws_bytes, ws_lowrank(T, K, rank))) return e;
+    return device_status(ttq::launch_lowrank(X, xt == TTQ_F32, T, K, ldx, A, B, M, rank, Y, yt == TTQ_F32,
+                                             ldy, (float*)ws, as_stream(stream)),
+                         "ttq_lowrank_add launch");
+}
+
+ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(a != nullptr, "args: null pointer");
+    TTQ_REQUIRE(dim_ok(a->T), "T out of range");
+    if (ttq_status e = check_quant_shape(a->M, a->K, a->bits, a->group)) return e;
+    if (ttq_status e = check_matrix("X", a->X, a->xt, a->T, a->K, a->ldx)) return e;
+    if (ttq_status e = check_matrix("W", a->W, a->wt, a->M, a->K, a->ldw)) return e;
+    if (ttq_status e = check_output(a->Y, a->yt, a->T, a->M, a->ldy)) return e;
+    if (ttq_status e = check_lowrank(a->B, a->A, a->rank, true)) return e;
+    TTQ_REQUIRE(std::isfinite(a->alpha) && a->alpha >= 0.f, "alpha must be finite and >= 0");
+    TTQ_REQUIRE(std::isfinite(a->lambda_rel) && a->lambda_rel >= 0.f, "lambda_rel must be finite and >= 0");
+    TTQ_REQUIRE(std::isfinite(a->p) && a->p > 0.f, "p must be finite and > 0");
+    if (a->p != 2.0f) return fail(TTQ_ERR_UNSUPPORTED, "only p = 2 (second-moment statistics) is implemented");
+    TTQ_REQUIRE(a->ssq == nullptr || aligned(a->ssq, 8), "ssq: not 8-byte aligned");
+    TTQ_REQUIRE(a->s == nullptr || aligned(a->s, 16), "s: not 16-byte aligned");
+    TTQ_REQUIRE(a->codes == nullptr || aligned(a->codes, 16), "codes: not 16-byte aligned");
+    TTQ_REQUIRE(a->scale_f16 == nullptr || aligned(a->scale_f16, 2), "scale_f16: misaligned");
+    TTQ_REQUIRE(a->zero_f16 == nullptr || aligned(a->zero_f16, 2), "zero_f16: misaligned");
+    if (a->T == 0) return TTQ_OK;   // no prompt tokens: nothing to estimate or project
+
+    const StateLayout L = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank);
+    if (ttq_status e = check_ws(ws, ws_bytes, L.total)) return e;
+    char* w = (char*)ws;
+    double* ssq = a->ssq ? a->ssq : (double*)(w + L.ssq);
+    float* s = a->s ? a->s : (float*)(w + L.s);
+    int32_t* codes = a->codes ? a->codes : (int32_t*)(w + L.codes);
+    uint16_t* scale = a->scale_f16 ? a->scale_f16 : (uint16_t*)(w + L.scale);
+    uint16_t* zero = a->zero_f16 ? a->zero_f16 : (uint16_t*)(w + L.zero);
+    void* scratch = w + L.scratch;
+    hipStream_t st = as_stream(stream);
+    const bool xf32 = a->xt == TTQ_F32;
+
+    if (ttq_status e = device_status(
+            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st), "stats"))
+        return e;
+    if (ttq_status e = device_status(
+            ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, s, st), "scales"))
+        return e;
+    if (a->M == 0) return TTQ_OK;
+    if (ttq_status e = device_status(
+            ttq::launch_quantize(a->W, a->wt == TTQ_F32, a->M, a->K, a->ldw, s, a->bits, a->group, a->B,
+                                 a->A, a->rank, (uint32_t*)codes, scale, zero, st),
+            "quantize"))
+        return e;
+    float* inv = (float*)scratch;
+    if (ttq_status e = device_status(ttq::launch_inv_scales(s, a->K, inv, st), "inv_scales")) return e;
+    if (ttq_status e = device_status(
+            ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, inv, (const uint32_t*)codes, scale, zero,
+                              a->M, a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, st),
+            "qgemm"))
+        return e;
+    if (a->rank > 0) {
+        if (ttq_status e = device_status(
+                ttq::launch_lowrank(a->X, xf32, a->T, a->K, a->ldx, a->A, a->B, a->M, a->rank, a->Y,
+                                    a->yt == TTQ_F32, a->ldy, (float*)scratch, st),
+                "lowrank"))
+            return e;
+    }
+    return TTQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+"""Thin ctypes binding of libttq (include/ttq.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libttq.so.  Tensors must be device (HIP) tensors; PyTorch supplies memory and
+the current stream.  There is no CPU fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttq.so")
+
+TTQ_OK, TTQ_ERR_INVALID, TTQ_ERR_UNSUPPORTED, TTQ_ERR_DEVICE = 0, 1, 2, 3
+TTQ_F32, TTQ_BF16 = 0, 1
+
+EXPORTS = ("ttq_stats", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm",
+           "ttq_lowrank_add", "ttq_workspace_bytes", "ttq_linear", "ttq_status_str",
+           "ttq_last_error")
+
+
+class TTQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class LinearArgs(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p), ("xt", ctypes.c_int), ("T", ctypes.c_int64),
+        ("K", ctypes.c_int64), ("ldx", ctypes.c_int64),
+        ("W", ctypes.c_void_p), ("wt", ctypes.c_int), ("M", ctypes.c_int64),
+        ("ldw", ctypes.c_int64),
+        ("alpha", ctypes.c_float), ("lambda_rel", ctypes.c_float), ("p", ctypes.c_float),
+        ("bits", ctypes.c_int), ("group", ctypes.c_int),
+        ("B", ctypes.c_void_p), ("A", ctypes.c_void_p), ("rank", ctypes.c_int),
+        ("Y", ctypes.c_void_p), ("yt", ctypes.c_int), ("ldy", ctypes.c_int64),
+        ("ssq", ctypes.c_void_p), ("s", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+        ("scale_f16", ctypes.c_void_p), ("zero_f16", ctypes.c_void_p),
+    ]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttq.so (once) and declare the C signatures."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m online_activation_aware_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "ttq_stats": [vp, i32, i64, i64, i64, vp, i32, vp, sz, vp],
+        "ttq_awq_scales": [vp, i64, i64, f32, f32, f32, vp, vp],
+        "ttq_quantize_groups": [vp, i32, i64, i64, i64, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp],
+        "ttq_qgemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, i32, i64, vp, sz, vp],
+        "ttq_lowrank_add": [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, i32, i64, vp, sz, vp],
+        "ttq_workspace_bytes": [i64, i64, i64, i32, i32, i32],
+        "ttq_linear": [ctypes.POINTER(LinearArgs), vp, sz, vp],
+        "ttq_status_str": [i32],
+        "ttq_last_error": [],
+    }
+    for name, argtypes in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    L.ttq_workspace_bytes.restype = ctypes.c_size_t
+    L.ttq_status_str.restype = ctypes.c_char_p
+    L.ttq_last_error.restype = ctypes.c_char_p
+    _lib_handle = L
+    return L
+
+
+# ------------------------------------------------------------------ helpers
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TTQ_F32
+    if t.dtype == torch.bfloat16:
+        return TTQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _ld(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride in its last dimension")
+    return t.stride(0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(status: int) -> None:
+    if status != TTQ_OK:
+        L = lib()
+        raise TTQError(status, f"{L.ttq_status_str(status).decode()}: {L.ttq_last_error().decode()}")
+
+
+def _ws(ws: Optional[torch.Tensor], device) -> tuple:
+    if ws is None:
+        return None, 0
+    if ws.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    return _dev(ws, "ws"), ws.numel()
+
+
+# ------------------------------------------------------------------ calls
+
+def ttq_workspace_bytes(T: int, K: int, M: int, bits: int, group: int, rank: int = 0) -> int:
+    return int(lib().ttq_workspace_bytes(T, K, M, bits, group, rank))
+
+
+def workspace(T: int, K: int, M: int, bits: int, group: int, rank: int = 0, device="cuda") -> torch.Tensor:
+    """Allocate a workspace tensor of ttq_workspace_bytes() bytes."""
+    n = ttq_workspace_bytes(T, K, M, bits, group, rank)
+    if n == 0:
+        raise ValueError("no call accepts these sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ttq_stats(X: torch.Tensor, ssq: torch.Tensor, accumulate: bool = False,
+              ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if ssq.dtype != torch.float64:
+        raise TypeError("ssq must be float64")
+    T, K = X.shape
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_stats(_dev(X, "X"), _dtype_code(X), T, K, _ld(X, "X"), _dev(ssq, "ssq"),
+                           int(bool(accumulate)), wp, wn, _stream(stream)))
+    return ssq
+
+
+def ttq_awq_scales(ssq: torch.Tensor, n_tokens: int, alpha: float, lambda_rel: float,
+                   p: float = 2.0, s: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    K = ssq.numel()
+    if s is None:
+        s = torch.empty(K, dtype=torch.float32, device=ssq.device)
+    _check(lib().ttq_awq_scales(_dev(ssq, "ssq"), n_tokens, K, alpha, lambda_rel, p, _dev(s, "s"),
+                                _stream(stream)))
+    return s
+
+
+def ttq_quantize_groups(W: torch.Tensor, s: Optional[torch.Tensor], bits: int, group: int,
+                        B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                        codes: Optional[torch.Tensor] = None, scale_f16: Optional[torch.Tensor] = None,
+                        zero_f16: Optional[torch.Tensor] = None, stream=None):
+    M, K = W.shape
+    rank = 0 if B is None else B.shape[1]
+    dev = W.device
+    if codes is None:
+        codes = torch.empty((M, K * bits // 32), dtype=torch.int32, device=dev)
+    if scale_f16 is None:
+        scale_f16 = torch.empty((M, K // group), dtype=torch.float16, device=dev)
+    if zero_f16 is None:
+        zero_f16 = torch.empty((M, K // group), dtype=torch.float16, device=dev)
+    _check(lib().ttq_quantize_groups(_dev(W, "W"), _dtype_code(W), M, K, _ld(W, "W"), _dev(s, "s"),
+                                     bits, group, _dev(B, "B"), _dev(A, "A"), rank, _dev(codes, "codes"),
+                                     _dev(scale_f16, "scale_f16"), _dev(zero_f16, "zero_f16"),
+                                     _stream(stream)))
+    return codes, scale_f16, zero_f16
+
+
+def ttq_qgemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: torch.Tensor,
+              zero_f16: torch.Tensor, M: int, bits: int, group: int, Y: Optional[torch.Tensor] = None,
+              y_dtype=torch.float32, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, K = X.shape
+    if Y is None:
+        Y = torch.empty((T, M), dtype=y_dtype, device=X.device)
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_qgemm(_dev(X, "X"), _dtype_code(X), T, K, _ld(X, "X"), _dev(s, "s"),
+                           _dev(codes, "codes"), _dev(scale_f16, "scale_f16"), _dev(zero_f16, "zero_f16"),
+                           M, bits, group, _dev(Y, "Y"), _dtype_code(Y), _ld(Y, "Y"), wp, wn,
+                           _stream(stream)))
+    return Y
+
+
+def ttq_lowrank_add(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, Y: torch.Tensor,
+                    ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, K = X.shape
+    M, rank = B.shape
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_lowrank_add(_dev(X, "X"), _dtype_code(X), T, K, _ld(X, "X"), _dev(A, "A"),
+                                 _dev(B, "B"), M, rank, _dev(Y, "Y"), _dtype_code(Y), _ld(Y, "Y"),
+                                 wp, wn, _stream(stream)))
+    return Y
+
+
+def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: float,
+               lambda_rel: float, p: float = 2.0, B: Optional[torch.Tensor] = None,
+               A: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
+               y_dtype=torch.float32, ws: Optional[torch.Tensor] = None, state: Optional[dict] = None,
+               stream=None) -> torch.Tensor:
+    """One call for the whole layer.  ``state`` may hold preallocated output
+    tensors ``ssq``, ``s``, ``codes``, ``scale_f16``, ``zero_f16`` that receive
+    the prompt's quantization state (for later decode-step ttq_qgemm calls)."""
+    T, K = X.shape
+    M = W.shape[0]
+    rank = 0 if B is None else B.shape[1]
+    if Y is None:
+        Y = torch.empty((T, M), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = workspace(T, K, M, bits, group, rank, device=X.device)
+    st = state or {}
+    a = LinearArgs(
+        X=_dev(X, "X"), xt=_dtype_code(X), T=T, K=K, ldx=_ld(X, "X"),
+        W=_dev(W, "W"), wt=_dtype_code(W), M=M, ldw=_ld(W, "W"),
+        alpha=alpha, lambda_rel=lambda_rel, p=p, bits=bits, group=group,
+        B=_dev(B, "B"), A=_dev(A, "A"), rank=rank,
+        Y=_dev(Y, "Y"), yt=_dtype_code(Y), ldy=_ld(Y, "Y"),
+        ssq=_dev(st.get("ssq"), "ssq"), s=_dev(st.get("s"), "s"), codes=_dev(st.get("codes"), "codes"),
+        scale_f16=_dev(st.get("scale_f16"), "scale_f16"), zero_f16=_dev(st.get("zero_f16"), "zero_f16"),
+    )
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_linear(ctypes.byref(a), wp, wn, _stream(stream)))
+    return Y
+
+
+def linear_state(T: int, K: int, M: int, bits: int, group: int, device="cuda") -> dict:
+    """Preallocated tensors for the quantization state ttq_linear can fill."""
+    return {
+        "ssq": torch.empty(K, dtype=torch.float64, device=device),
+        "s": torch.empty(K, dtype=torch.float32, device=device),
+        "codes": torch.empty((M, K * bits // 32), dtype=torch.int32, device=device),
+        "scale_f16": torch.empty((M, K // group), dtype=torch.float16, device=device),
+        "zero_f16": torch.empty((M, K // group), dtype=torch.float16, device=device),
+    }

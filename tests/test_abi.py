@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/ttq.h declares, and rejects malformed arguments on the host
+before any HIP call (fake, never-dereferenced device addresses are used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ttq.h")
+LIBPATH = os.path.join(ROOT, "online_activation_aware_amd", "libttq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libttq.so not built")
+
+FAKE = 0x100000  # 1 MiB: 256-byte aligned, never dereferenced by the failing calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    from online_activation_aware_amd import ttq
+    return ttq.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_all_exported(L):
+    from online_activation_aware_amd import ttq
+    names = header_functions()
+    assert set(names) == set(ttq.EXPORTS)
+    raw = ctypes.CDLL(LIBPATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(L):
+    assert L.ttq_status_str(0) == b"TTQ_OK"
+    assert L.ttq_status_str(1) == b"TTQ_ERR_INVALID"
+    assert L.ttq_status_str(2) == b"TTQ_ERR_UNSUPPORTED"
+    assert L.ttq_status_str(3) == b"TTQ_ERR_DEVICE"
+    assert L.ttq_status_str(99) == b"TTQ_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(L):
+    from online_activation_aware_amd import ttq
+    n = ttq.ttq_workspace_bytes(2048, 4096, 4096, 4, 32, 0)
+    # at least the quantization state: ssq + s + codes + steps + zeros
+    state = 4096 * 8 + 4096 * 4 + 4096 * 4096 * 4 // 8 + 2 * 4096 * 128 * 2
+    assert n >= state and n % 256 == 0
+    assert ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 16) >= ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 0)
+    for bad in [(10, 100, 10, 4, 32, 0),     # K not a multiple of 32
+                (10, 128, 10, 6, 32, 0),     # bits
+                (10, 128, 10, 4, 48, 0),     # group
+                (10, 96, 10, 4, 64, 0),      # group does not divide K
+                (10, 128, 10, 4, 32, 33),    # rank
+                (-1, 128, 10, 4, 32, 0)]:
+        assert ttq.ttq_workspace_bytes(*bad) == 0
+
+
+def _err(L):
+    return L.ttq_last_error().decode()
+
+
+def test_stats_rejects(L):
+    st = L.ttq_stats
+    assert st(FAKE, 1, 16, 100, 100, FAKE, 0, FAKE, 1 << 30, None) == 1   # K % 8
+    assert "K" in _err(L)
+    assert st(FAKE, 5, 16, 128, 128, FAKE, 0, FAKE, 1 << 30, None) == 1   # dtype
+    assert st(FAKE, 1, 16, 128, 64, FAKE, 0, FAKE, 1 << 30, None) == 1    # ldx < K
+    assert st(FAKE + 2, 1, 16, 128, 128, FAKE, 0, FAKE, 1 << 30, None) == 1  # X alignment
+    assert st(FAKE, 1, 16, 128, 132, FAKE, 0, FAKE, 1 << 30, None) == 1   # stride bytes
+    assert st(None, 1, 16, 128, 128, FAKE, 0, FAKE, 1 << 30, None) == 1   # null X
+    assert st(FAKE, 1, 16, 128, 128, None, 0, FAKE, 1 << 30, None) == 1   # null ssq
+    assert st(FAKE, 1, 16, 128, 128, FAKE, 0, FAKE, 8, None) == 1         # workspace too small
+    assert "workspace" in _err(L)
+    assert st(FAKE, 1, 16, 128, 128, FAKE, 0, FAKE + 16, 1 << 30, None) == 1  # ws alignment
+
+
+def test_scales_rejects(L):
+    sc = L.ttq_awq_scales
+    assert sc(FAKE, 0, 128, 0.5, 0.01, 2.0, FAKE, None) == 1               # n_tokens
+    assert sc(FAKE, 4, 128, -0.5, 0.01, 2.0, FAKE, None) == 1              # alpha < 0
+    assert sc(FAKE, 4, 128, float("nan"), 0.01, 2.0, FAKE, None) == 1      # alpha NaN
+    assert sc(FAKE, 4, 128, 0.5, float("inf"), 2.0, FAKE, None) == 1       # lambda
+    assert sc(FAKE, 4, 128, 0.5, 0.01, 1.0, FAKE, None) == 2               # p != 2
+    assert "p = 2" in _err(L)
+    assert sc(FAKE, 4, 128, 0.5, 0.01, 2.0, FAKE + 4, None) == 1           # s alignment
+
+
+def test_quantize_rejects(L):
+    q = L.ttq_quantize_groups
+    ok = dict(W=FAKE, wt=1, M=64, K=256, ldw=256, s=FAKE, bits=4, group=32, B=None, A=None, rank=0,
+              codes=FAKE, scale=FAKE, zero=FAKE, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return q(*a.values())
+    assert call(bits=1) == 1 and call(bits=6) == 1
+    assert call(group=8) == 1 and call(group=256) == 1
+    assert call(K=96, ldw=96, group=64) == 1           # group does not divide K
+    assert call(K=48, ldw=48, group=16) == 1           # K not a multiple of 32
+    assert call(rank=4) == 1                           # rank without factors
+    assert call(rank=0, B=FAKE, A=FAKE) == 1           # factors without rank
+    assert call(rank=40, B=FAKE, A=FAKE) == 1          # rank above the limit
+    assert call(codes=None) == 1
+    assert call(s=FAKE + 4) == 1
+    assert call(M=-1) == 1
+    assert call(M=0) == 0                               # empty: nothing to do
+
+
+def test_qgemm_rejects(L):
+    g = L.ttq_qgemm
+    ok = dict(X=FAKE, xt=1, T=8, K=256, ldx=256, s=FAKE, codes=FAKE, scale=FAKE, zero=FAKE, M=64,
+              bits=4, group=32, Y=FAKE, yt=0, ldy=64, ws=FAKE, wsb=1 << 20, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(*a.values())
+    assert call(ldy=32) == 1                            # ldy < M
+    assert call(Y=FAKE + 2) == 1                        # fp32 Y not 4-byte aligned
+    assert call(ldx=260) == 1                           # X rows (520 B) not a multiple of 16 bytes
+    assert call(s=None) == 1
+    assert call(ws=None) == 1
+    assert call(wsb=16) == 1
+    assert call(yt=7) == 1
+    assert call(T=0) == 0 and call(M=0) == 0            # empty calls
+
+
+def test_lowrank_and_linear_reject(L):
+    from online_activation_aware_amd import ttq
+    assert L.ttq_lowrank_add(FAKE, 1, 8, 256, 256, FAKE, FAKE, 64, 0, FAKE, 0, 64, FAKE, 1 << 20, None) == 1
+    assert L.ttq_lowrank_add(FAKE, 1, 8, 256, 256, None, FAKE, 64, 4, FAKE, 0, 64, FAKE, 1 << 20, None) == 1
+    assert L.ttq_linear(None, FAKE, 1 << 20, None) == 1
+    a = ttq.LinearArgs(X=FAKE, xt=1, T=8, K=256, ldx=256, W=FAKE, wt=1, M=64, ldw=256, alpha=0.5,
+                       lambda_rel=0.01, p=3.0, bits=4, group=32, B=None, A=None, rank=0, Y=FAKE, yt=0,
+                       ldy=64)
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 2   # p != 2
+    a.p = 2.0
+    a.bits = 9
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1
+    a.bits = 4
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 16, None) == 1         # workspace too small
+    a.T = 0
+    assert L.ttq_linear(ctypes.byref(a), None, 0, None) == 0          # empty prompt

@@ -1,0 +1,339 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Sizes here span several tiles with ragged tails; tests/test_gpu_fullsize.py
+covers the benchmark workloads at full size on sampled outputs.
+Bars: fp64 statistics to 1e-12 relative; scales within 1e-5 relative; fp16
+steps and zero points exact; codes exact except where the oracle's
+pre-rounding value lies within 1e-4 of a step of a rounding boundary; the
+layer output Y within 2e-3 relative Frobenius error (fp32 Y).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import bf16_bits_to_f64, f16_dev, f32_dev, host, i32_dev, rel_fro, say, to_dev
+from online_activation_aware_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-3          # relative Frobenius error of Y (fp32 output)
+Y_TOL_BF16_OUT = 4e-3  # bf16 output adds one more bf16 rounding (~1.5e-3 in quadrature)
+S_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def T():
+    from online_activation_aware_amd import ttq
+    ttq.lib()
+    return ttq
+
+
+def _inputs(key, seed=None, **sizes):
+    wl = synth.workload(key, **sizes)
+    return wl, synth.make_inputs(wl, seed=seed)
+
+
+def _check_codes(T, got_codes, or_q, or_u, bits, K):
+    gq = oracle.unpack_codes(got_codes, bits, K)
+    band = oracle.boundary_band(or_u)
+    bad = (gq != or_q) & ~band
+    assert not bad.any(), f"{int(bad.sum())} codes differ outside the rounding band"
+    # the GPU's words are a valid packing of its codes (layout round trip)
+    np.testing.assert_array_equal(oracle.pack_codes(gq, bits), got_codes)
+    return int(((gq != or_q) & band).sum())
+
+
+# ------------------------------------------------------------------ stats
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("Tn,K", [(1, 512), (77, 1000), (300, 2056), (1031, 4104)])
+def test_stats_parity(T, xdt, Tn, K):
+    say(f"stats xdt={xdt} T={Tn} K={K}")
+    rng = np.random.default_rng(Tn + K)
+    X = synth.encode(rng.standard_normal((Tn, K)) * rng.lognormal(0, 1, K)[None, :], xdt)
+    ref = oracle.stats(X, xdt)
+    ws = torch.empty(Tn * K * 8 + 4096, dtype=torch.uint8, device="cuda")  # >= chunks * K * 8
+    ssq = torch.empty(K, dtype=torch.float64, device="cuda")
+    T.ttq_stats(to_dev(X, xdt), ssq, ws=ws)
+    np.testing.assert_allclose(host(ssq), ref, rtol=1e-12, atol=0)
+
+
+def test_stats_accumulate_and_strided(T):
+    say("stats accumulate + strided rows")
+    rng = np.random.default_rng(5)
+    K = 768
+    X = synth.encode(rng.standard_normal((200, K)), "bf16")
+    big = torch.zeros((200, K + 64), dtype=torch.bfloat16, device="cuda")
+    big[:, :K] = to_dev(X, "bf16")
+    ws = T.workspace(200, K, 32, 4, 32)
+    ssq = torch.full((K,), 7.0, dtype=torch.float64, device="cuda")
+    T.ttq_stats(big[:120, :K], ssq, accumulate=False, ws=ws)
+    T.ttq_stats(big[120:, :K], ssq, accumulate=True, ws=ws)
+    ref = oracle.stats(X[120:], "bf16", oracle.stats(X[:120], "bf16"))
+    np.testing.assert_allclose(host(ssq), ref, rtol=1e-12)
+
+
+# ------------------------------------------------------------------ scales
+
+@pytest.mark.parametrize("K", [32, 768, 4096, 14336])
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0])
+def test_scales_parity(T, K, alpha):
+    say(f"scales K={K} alpha={alpha}")
+    rng = np.random.default_rng(K)
+    ssq = rng.lognormal(3, 2, K) * 100
+    ssq[::97] = 0.0
+    ref = oracle.awq_scales(ssq, 123, alpha, 1e-2)
+    s = T.ttq_awq_scales(torch.from_numpy(ssq).to("cuda"), 123, alpha, 1e-2)
+    got = host(s)
+    np.testing.assert_allclose(got, ref, rtol=S_TOL)
+    assert np.mean(got == ref) > 0.99
+    if alpha == 0.0:
+        np.testing.assert_array_equal(got, np.ones(K, np.float32))
+
+
+def test_scales_zero_input_is_one(T):
+    s = T.ttq_awq_scales(torch.zeros(256, dtype=torch.float64, device="cuda"), 8, 0.5, 1e-2)
+    np.testing.assert_array_equal(host(s), np.ones(256, np.float32))
+
+
+def test_scales_unsupported_p(T):
+    with pytest.raises(T.TTQError) as e:
+        T.ttq_awq_scales(torch.ones(64, dtype=torch.float64, device="cuda"), 8, 0.5, 1e-2, p=1.0)
+    assert e.value.status == T.TTQ_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+@pytest.mark.parametrize("bits,group", [(b, g) for b in (2, 3, 4, 5) for g in (16, 32, 64, 128)])
+def test_quantize_parity(T, wdt, bits, group):
+    say(f"quantize wdt={wdt} bits={bits} group={group}")
+    M, K = 136, 1152
+    rng = np.random.default_rng(bits * 1000 + group)
+    W = synth.encode(rng.standard_normal((M, K)) * 0.02, wdt)
+    s = (rng.lognormal(0, 0.7, K)).astype(np.float32)
+    v = oracle.quant_values(W, wdt, s)
+    r = oracle.group_rtn(v, bits, group)
+    codes, sc, zz = T.ttq_quantize_groups(to_dev(W, wdt), f32_dev(s), bits, group)
+    np.testing.assert_array_equal(host(sc), r["delta"])
+    np.testing.assert_array_equal(host(zz), r["zero"])
+    _check_codes(T, host(codes), r["q"], r["u"], bits, K)
+
+
+def test_quantize_without_scales_is_plain_rtn(T):
+    say("quantize s=NULL")
+    M, K = 64, 512
+    rng = np.random.default_rng(9)
+    W = synth.encode(rng.standard_normal((M, K)) * 0.05, "bf16")
+    r = oracle.group_rtn(oracle.quant_values(W, "bf16", np.ones(K, np.float32)), 4, 32)
+    codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "bf16"), None, 4, 32)
+    np.testing.assert_array_equal(host(sc), r["delta"])
+    np.testing.assert_array_equal(host(zz), r["zero"])
+    _check_codes(T, host(codes), r["q"], r["u"], 4, K)
+
+
+def test_quantize_degenerate_groups(T):
+    say("quantize zero / constant / one-sided groups")
+    M, K = 8, 256
+    W = np.zeros((M, K), np.float32)
+    W[1] = 0.25                       # constant positive row
+    W[2] = -0.5                       # constant negative row
+    W[3, :32] = np.linspace(0, 1, 32)  # one-sided group
+    W[4, 100] = 3.0                   # a lone spike
+    r = oracle.group_rtn(oracle.quant_values(W, "f32", np.ones(K, np.float32)), 3, 32)
+    codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "f32"), f32_dev(np.ones(K)), 3, 32)
+    np.testing.assert_array_equal(host(sc), r["delta"])
+    np.testing.assert_array_equal(host(zz), r["zero"])
+    _check_codes(T, host(codes), r["q"], r["u"], 3, K)
+
+
+@pytest.mark.parametrize("bits,group,rank", [(2, 32, 16), (3, 16, 8), (4, 64, 5), (5, 32, 32)])
+def test_quantize_lowrank_parity(T, bits, group, rank):
+    say(f"quantize lowrank bits={bits} group={group} rank={rank}")
+    wl, d = _inputs("c5", T=32, K=1024, M=96)
+    s = oracle.awq_scales(oracle.stats(d["X"], "bf16"), 32, 0.5, 1e-2)
+    B, A = oracle.lowrank_factors(d["W"], "bf16", s, rank)
+    v = oracle.quant_values(d["W"], "bf16", s, B, A)
+    r = oracle.group_rtn(v, bits, group)
+    codes, sc, zz = T.ttq_quantize_groups(to_dev(d["W"], "bf16"), f32_dev(s), bits, group,
+                                          B=f32_dev(B), A=f32_dev(A))
+    np.testing.assert_array_equal(host(sc), r["delta"])
+    np.testing.assert_array_equal(host(zz), r["zero"])
+    _check_codes(T, host(codes), r["q"], r["u"], bits, 1024)
+
+
+# ------------------------------------------------------------------ qgemm
+
+def _qgemm_case(T, key, Tn, K, M, bits, group, xdt, ydt, seed=0):
+    wl, d = _inputs(key, seed=seed, T=Tn, K=K, M=M)
+    X, W = d["X"], d["W"]
+    s = oracle.awq_scales(oracle.stats(X, xdt), Tn, 0.5, 1e-2)
+    r = oracle.group_rtn(oracle.quant_values(W, wl.wdtype, s), bits, group)
+    w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], group)
+    ref = oracle.project(X, xdt, s, w_hat)
+    codes = oracle.pack_codes(r["q"], bits)
+    ws = T.workspace(Tn, K, M, bits, group)
+    Y = T.ttq_qgemm(to_dev(X, xdt), f32_dev(s), i32_dev(codes), f16_dev(r["delta"]), f16_dev(r["zero"]),
+                    M, bits, group, y_dtype=torch.float32 if ydt == "f32" else torch.bfloat16, ws=ws)
+    got = host(Y)
+    got = got.astype(np.float64) if ydt == "f32" else bf16_bits_to_f64(got)
+    return got, ref
+
+
+@pytest.mark.parametrize("bits,group,K", [(4, 32, 1056), (3, 16, 1056), (2, 64, 1088), (5, 128, 1152),
+                                          (4, 16, 1024), (3, 128, 1024)])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_qgemm_parity(T, bits, group, K, xdt):
+    key = "c1" if xdt == "f32" else "c2"
+    say(f"qgemm bits={bits} group={group} K={K} xdt={xdt}")
+    got, ref = _qgemm_case(T, key, 200, K, 300, bits, group, xdt, "f32")
+    err = rel_fro(got, ref)
+    assert err < (Y_TOL if xdt == "bf16" else 1e-4), err
+
+
+@pytest.mark.parametrize("Tn,M", [(1, 128), (5, 302), (129, 130), (16, 64)])
+def test_qgemm_ragged_and_bf16_output(T, Tn, M):
+    say(f"qgemm ragged T={Tn} M={M}")
+    for ydt, tol in (("f32", Y_TOL), ("bf16", Y_TOL_BF16_OUT)):
+        got, ref = _qgemm_case(T, "c2", Tn, 512, M, 4, 32, "bf16", ydt, seed=Tn)
+        assert rel_fro(got, ref) < tol
+
+
+def test_qgemm_identity_input_layout(T):
+    # X = I: Y[t][o] = bf16((q - z) * step / s_t), element by element.
+    say("qgemm identity layout")
+    K, M = 256, 96
+    rng = np.random.default_rng(3)
+    W = synth.encode(rng.standard_normal((M, K)) * 0.05, "bf16")
+    s = rng.lognormal(0, 0.5, K).astype(np.float32)
+    r = oracle.group_rtn(oracle.quant_values(W, "bf16", s), 4, 32)
+    w_eff = oracle.dequant(r["q"], r["delta"], r["zero"], 32) / s.astype(np.float64)[None, :]
+    X = synth.encode(np.eye(K), "bf16")
+    ws = T.workspace(K, K, M, 4, 32)
+    Y = T.ttq_qgemm(to_dev(X, "bf16"), f32_dev(s), i32_dev(oracle.pack_codes(r["q"], 4)),
+                    f16_dev(r["delta"]), f16_dev(r["zero"]), M, 4, 32, ws=ws)
+    got = host(Y).astype(np.float64)
+    np.testing.assert_allclose(got, w_eff.T, rtol=2.0 ** -8, atol=1e-30)
+
+
+# ---------------------------------------------------------------- lowrank
+
+@pytest.mark.parametrize("xdt,rank", [("bf16", 16), ("f32", 7), ("bf16", 32)])
+def test_lowrank_add_parity(T, xdt, rank):
+    say(f"lowrank_add xdt={xdt} rank={rank}")
+    rng = np.random.default_rng(rank)
+    Tn, K, M = 150, 512, 200
+    X = synth.encode(rng.standard_normal((Tn, K)), xdt)
+    A = (rng.standard_normal((rank, K)) * 0.05).astype(np.float32)
+    B = (rng.standard_normal((M, rank))).astype(np.float32)
+    Y0 = rng.standard_normal((Tn, M)).astype(np.float32)
+    x = oracle.decode(X, xdt)
+    ref = Y0.astype(np.float64) + (x @ A.astype(np.float64).T) @ B.astype(np.float64).T
+    Y = f32_dev(Y0)
+    ws = T.workspace(Tn, K, M, 2, 32, rank)
+    T.ttq_lowrank_add(to_dev(X, xdt), f32_dev(A), f32_dev(B), Y, ws=ws)
+    assert rel_fro(host(Y), ref) < 1e-5
+
+
+# ------------------------------------------------------------ end to end
+
+E2E = [
+    ("c1", dict()),
+    ("c2", dict(T=160, K=1024, M=288)),
+    ("c3", dict(T=96, K=1024, M=320)),
+    ("c4", dict(T=100, K=2048, M=256)),
+    ("c5", dict(T=128, K=512, M=512)),
+]
+
+
+def _run_linear(T, wl, d, B=None, A=None):
+    dev_x = to_dev(d["X"], wl.xdtype)
+    dev_w = to_dev(d["W"], wl.wdtype)
+    st = T.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    Y = T.ttq_linear(dev_x, dev_w, wl.bits, wl.group, wl.alpha, wl.lambda_rel,
+                     B=None if B is None else f32_dev(B), A=None if A is None else f32_dev(A), state=st)
+    return Y, st
+
+
+@pytest.mark.parametrize("key,sizes", E2E, ids=[k for k, _ in E2E])
+def test_linear_end_to_end(T, key, sizes):
+    say(f"linear e2e {key} {sizes}")
+    wl, d = _inputs(key, **sizes)
+    B = A = None
+    if wl.rank:
+        s0 = oracle.awq_scales(oracle.stats(d["X"], wl.xdtype), wl.T, wl.alpha, wl.lambda_rel)
+        B, A = oracle.lowrank_factors(d["W"], wl.wdtype, s0, wl.rank)
+    ref = oracle.linear(d["X"], wl.xdtype, d["W"], wl.wdtype, wl.bits, wl.group, wl.alpha,
+                        wl.lambda_rel, B=B, A=A)
+    Y, st = _run_linear(T, wl, d, B, A)
+    np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
+    s = host(st["s"])
+    np.testing.assert_allclose(s, ref["s"], rtol=S_TOL)
+    if np.array_equal(s, ref["s"]):   # identical scales: the quantizer must agree too
+        np.testing.assert_array_equal(host(st["scale_f16"]), ref["delta"])
+        np.testing.assert_array_equal(host(st["zero_f16"]), ref["zero"])
+        _check_codes(T, host(st["codes"]), ref["q"], ref["u"], wl.bits, wl.K)
+    err = rel_fro(host(Y), ref["Y"])
+    say(f"  Y rel err {err:.3e}")
+    assert err < Y_TOL
+
+
+def test_decode_steps_reuse_prompt_state(T):
+    say("decode steps")
+    wl, d = _inputs("c4", T=64, K=2048, M=256, decode_T=(1, 4, 16))
+    ref = oracle.linear(d["X"], "bf16", d["W"], "bf16", wl.bits, wl.group, wl.alpha, wl.lambda_rel)
+    _, st = _run_linear(T, wl, d)
+    ws = T.workspace(16, wl.K, wl.M, wl.bits, wl.group)
+    for td, Xd in d["X_decode"].items():
+        Yd = T.ttq_qgemm(to_dev(Xd, "bf16"), st["s"], st["codes"], st["scale_f16"], st["zero_f16"],
+                         wl.M, wl.bits, wl.group, ws=ws)
+        refd = oracle.project(Xd, "bf16", ref["s"], ref["w_hat"])
+        assert rel_fro(host(Yd), refd) < Y_TOL, td
+
+
+def test_run_twice_bitwise_identical(T):
+    say("determinism")
+    wl, d = _inputs("c3", T=96, K=1024, M=320)
+    Y1, st1 = _run_linear(T, wl, d)
+    Y2, st2 = _run_linear(T, wl, d)
+    assert torch.equal(Y1, Y2)
+    for k in st1:
+        assert torch.equal(st1[k], st2[k]), k
+
+
+def test_linear_strided_operands(T):
+    say("linear strided X/W/Y")
+    wl, d = _inputs("c2", T=70, K=512, M=200)
+    X = torch.zeros((70, 512 + 64), dtype=torch.bfloat16, device="cuda")
+    X[:, :512] = to_dev(d["X"], "bf16")
+    W = torch.zeros((200, 512 + 32), dtype=torch.bfloat16, device="cuda")
+    W[:, :512] = to_dev(d["W"], "bf16")
+    Yb = torch.full((70, 200 + 28), 5.0, dtype=torch.float32, device="cuda")
+    T.ttq_linear(X[:, :512], W[:, :512], wl.bits, wl.group, wl.alpha, wl.lambda_rel, Y=Yb[:, :200])
+    ref = oracle.linear(d["X"], "bf16", d["W"], "bf16", wl.bits, wl.group, wl.alpha, wl.lambda_rel)
+    got = host(Yb)
+    assert rel_fro(got[:, :200], ref["Y"]) < Y_TOL
+    assert np.all(got[:, 200:] == 5.0)   # padding columns untouched
+
+
+def test_empty_calls_are_noops(T):
+    say("empty calls")
+    Y = torch.full((0, 64), 1.0, device="cuda")
+    X = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    T.ttq_linear(X, W, 4, 32, 0.5, 1e-2, Y=Y, ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    ssq = torch.full((256,), 3.0, dtype=torch.float64, device="cuda")
+    T.ttq_stats(X, ssq, accumulate=True)
+    assert torch.all(ssq == 3.0)
+    T.ttq_stats(X, ssq, accumulate=False)
+    assert torch.all(ssq == 0.0)
+
+
+def test_binding_raises_on_bad_arguments(T):
+    X = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((8, 100), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises((T.TTQError, ValueError)):
+        T.ttq_linear(X, W, 4, 32, 0.5, 1e-2)
+    with pytest.raises(TypeError):
+        T.ttq_stats(torch.zeros((4, 64)), torch.zeros(64, dtype=torch.float64))
