@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTQ per-prompt layer path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the whole per-prompt path for one linear layer —
+activation statistics -> shrunk AWQ scales -> group RTN of the scaled weight
+-> quantized projection (plus the low-rank term when the workload has one) —
+through the C ABI's ttq_linear, on synthetic inputs already resident in HBM.
+Inputs rotate over several copies (>= 768 MiB in total) so that successive
+steps do not find X and W in the 256 MiB Infinity Cache.
+
+Prints one JSON line (stdout): the layer time in microseconds, the roofline
+of the dominant kernel (the quantized GEMM) from HIP events on the launch
+stream, the per-stage breakdown, and the CPU oracle timed on the host.
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ttq_linear µs/layer (stats+quant+qGEMM); qGEMM TFLOP/s; HBM GB/s vs peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+
+# HBM bytes per qGEMM launch measured with rocprofv3 --pmc (FETCH_SIZE and
+# WRITE_SIZE, scaled by the factor a plain copy of known size gives), keyed by
+# the SHA-256 of the kernel source they were taken on.  A source change
+# invalidates them (traffic is then reported as null).
+MEASURED_TRAFFIC = {}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    path = os.path.join(ROOT, "online_activation_aware_amd", "csrc", "qgemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def esize(dt: str) -> int:
+    return 4 if dt == "f32" else 2
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes each kernel must move at minimum (Y in fp32)."""
+    T, K, M, b, g = wl.T, wl.K, wl.M, wl.bits, wl.group
+    codes = M * K * b // 8
+    steps = 2 * M * (K // g) * 2
+    return {
+        "stats": T * K * esize(wl.xdtype) + K * 8,
+        "scales": K * 8 + K * 4,
+        "quantize": M * K * esize(wl.wdtype) + K * 4 + codes + steps
+        + (wl.rank * (M + K) * 4 if wl.rank else 0),
+        "qgemm": T * K * esize(wl.xdtype) + K * 4 + codes + steps + T * M * 4,
+    }
+
+
+def harness_lowrank_factors(W64, s, rank, seed=0):
+    """Input preparation for low-rank workloads (not timed): top-`rank`
+    factors of W diag(s) by randomized subspace iteration, B = U S,
+    A = V^T diag(1/s), in fp32."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    s64 = s.astype(np.float64)
+    Ws = W64 * s64[None, :]
+    Q = np.linalg.qr(Ws @ rng.standard_normal((Ws.shape[1], rank + 8)))[0]
+    for _ in range(4):
+        Q = np.linalg.qr(Ws @ (Ws.T @ Q))[0]
+    U, S, Vt = np.linalg.svd(Q.T @ Ws, full_matrices=False)
+    U = Q @ U
+    B = (U[:, :rank] * S[None, :rank]).astype(np.float32)
+    A = (Vt[:rank] / s64[None, :]).astype(np.float32)
+    return B, A
+
+
+def cpu_baseline(wl, data, B=None, A=None) -> dict:
+    """The CPU oracle, as it stands, timed on this host on the same layer."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 9 and (len(times) < 3 or time.perf_counter() - t_start < 10.0):
+        t0 = time.perf_counter()
+        ssq = oracle.stats(data["X"], wl.xdtype)
+        s = oracle.awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel)
+        v = oracle.quant_values(data["W"], wl.wdtype, s, B, A)
+        r = oracle.group_rtn(v, wl.bits, wl.group)
+        oracle.pack_codes(r["q"], wl.bits)
+        w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], wl.group)
+        Y = oracle.project(data["X"], wl.xdtype, s, w_hat, B, A)
+        times.append(time.perf_counter() - t0)
+        assert np.isfinite(Y).all()
+    dt = float(np.median(times))
+    return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full layer ({wl.T}x{wl.K}->{wl.M}) through the fp64 numpy oracle (stats, scales, "
+                      f"quantize, pack, dequantize, projection), median of {len(times)} runs "
+                      f"({sum(times):.1f} s of CPU work); cores = BLAS threads"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: 4096->4096, T=2048)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-mib", type=int, default=768)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (for HBM counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the path needs no cross-GPU exchange and each GPU runs it independently.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from online_activation_aware_amd import synth, ttq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return 0
+
+    ttq.lib()  # fail loudly if the HIP library is missing
+    wl = synth.workload(args.workload)
+    log(f"workload {wl.key}: {wl.name}")
+    data = synth.make_inputs(wl)
+
+    def to_dev(a, dt):
+        t = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16) if dt == "bf16"
+             else torch.from_numpy(np.ascontiguousarray(a)))
+        return t.to(dev)
+
+    X0, W0 = to_dev(data["X"], wl.xdtype), to_dev(data["W"], wl.wdtype)
+    per_copy = X0.numel() * X0.element_size() + W0.numel() * W0.element_size()
+    ncopy = max(2, min(64, math.ceil((args.min_rotation_mib << 20) / per_copy)))
+    Xs = [X0] + [X0.clone() for _ in range(ncopy - 1)]
+    Ws = [W0] + [W0.clone() for _ in range(ncopy - 1)]
+    log(f"{ncopy} rotating input copies ({ncopy * per_copy / 2**20:.0f} MiB)")
+
+    B = A = None
+    B_h = A_h = None
+    if wl.rank:
+        ssq = torch.empty(wl.K, dtype=torch.float64, device=dev)
+        ttq.ttq_stats(X0, ssq, ws=ttq.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, wl.rank, device=dev))
+        s0 = ttq.ttq_awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel).cpu().numpy()
+        w64 = synth.as_float(data["W"], wl.wdtype).astype(np.float64)
+        B_h, A_h = harness_lowrank_factors(w64, s0, wl.rank)
+        B, A = torch.from_numpy(B_h).to(dev), torch.from_numpy(A_h).to(dev)
+        log("low-rank factors prepared (harness, untimed)")
+
+    st = ttq.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group, device=dev)
+    ws = ttq.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, wl.rank, device=dev)
+    Y = torch.empty((wl.T, wl.M), dtype=torch.float32, device=dev)
+
+    def step(i):
+        ttq.ttq_linear(Xs[i % ncopy], Ws[i % ncopy], wl.bits, wl.group, wl.alpha, wl.lambda_rel,
+                       B=B, A=A, Y=Y, ws=ws, state=st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/layer (wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
+
+    # Per-stage breakdown: the same kernels through the individual entry points,
+    # each bracketed by events on the launch stream.
+    stages = ["stats", "scales", "quantize", "qgemm"] + (["lowrank"] if wl.rank else [])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        X, W = Xs[i % ncopy], Ws[i % ncopy]
+        ev = evs[i]
+        ev[0].record()
+        ttq.ttq_stats(X, st["ssq"], ws=ws)
+        ev[1].record()
+        ttq.ttq_awq_scales(st["ssq"], wl.T, wl.alpha, wl.lambda_rel, s=st["s"])
+        ev[2].record()
+        ttq.ttq_quantize_groups(W, st["s"], wl.bits, wl.group, B=B, A=A, codes=st["codes"],
+                                scale_f16=st["scale_f16"], zero_f16=st["zero_f16"])
+        ev[3].record()
+        ttq.ttq_qgemm(X, st["s"], st["codes"], st["scale_f16"], st["zero_f16"], wl.M, wl.bits, wl.group,
+                      Y=Y, ws=ws)
+        ev[4].record()
+        if wl.rank:
+            ttq.ttq_lowrank_add(X, A, B, Y, ws=ws)
+            ev[5].record()
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, name in enumerate(stages)}
+    alg = algorithmic_bytes(wl)
+    flops = 2.0 * wl.T * wl.M * wl.K
+    q_s = stage_ms["qgemm"] * 1e-3
+    achieved = flops / q_s / 1e12
+    h = kernel_source_hash()
+    traffic = MEASURED_TRAFFIC.get(h)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "k_qgemm (dequantize codes into LDS -> bf16 MFMA 16x16x32, fp32 accumulate)",
+                "flops_per_launch": flops, "avg_launch_us": round(stage_ms["qgemm"] * 1e3, 2)}
+    breakdown = {}
+    for name in stages:
+        us = stage_ms[name] * 1e3
+        d = {"us": round(us, 2)}
+        if name in alg:
+            d["alg_bytes"] = alg[name]
+            d["gbs"] = round(alg[name] / (us * 1e-6) / 1e9, 1)
+            d["hbm_frac"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        breakdown[name] = d
+    breakdown["qgemm"]["tflops"] = round(achieved, 2)
+    for name, d in breakdown.items():
+        log(f"  {name:9s} {d['us']:8.2f} us" + (f"  {d['gbs']:8.1f} GB/s" if "gbs" in d else ""))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same layer ...")
+        cpu = cpu_baseline(wl, data, B_h, A_h)
+        log(f"  oracle: {cpu['value'] / 1e6:.2f} s/layer on {cpu['cores']} BLAS threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms * 1e3, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "K": wl.K, "M": wl.M, "bits": wl.bits, "group": wl.group,
+                   "alpha": wl.alpha, "lambda_rel": wl.lambda_rel, "rank": wl.rank, "x_dtype": wl.xdtype,
+                   "w_dtype": wl.wdtype, "y_dtype": "f32",
+                   "cache": f"{ncopy} rotating copies of X and W ({ncopy * per_copy / 2**20:.0f} MiB)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

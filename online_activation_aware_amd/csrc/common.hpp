@@ -28,9 +28,12 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t packed) {
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
-// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32 (RNE).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // fp16 bit pattern <-> fp32.

@@ -16,13 +16,12 @@ hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t 
                         int accumulate, double* part, hipStream_t st);
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float* s, hipStream_t st);
-hipError_t launch_inv_scales(const float* s, int64_t K, float* inv, hipStream_t st);
 hipError_t launch_quantize(const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw,
                            const float* s, int bits, int group, const float* B, const float* A,
                            int rank, uint32_t* codes, uint16_t* scale, uint16_t* zero,
                            hipStream_t st);
 hipError_t launch_qgemm(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
-                        const float* inv_s, const uint32_t* codes, const uint16_t* scale,
+                        const float* s, const uint32_t* codes, const uint16_t* scale,
                         const uint16_t* zero, int64_t M, int bits, int group, void* Y, bool yf32,
                         int64_t ldy, hipStream_t st);
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,

@@ -19,13 +19,78 @@ namespace ttq {
 constexpr int kQThreads = 256;
 constexpr int kQChans = kWave * 8;
 
+// Group RTN of one lane's 8 values and packing of the quad's 32 codes.
+// All 64 lanes of the wave must call this together (it shuffles).
+template <int BITS, int GROUP>
+__device__ __forceinline__ void quantize_and_store(const float (&v)[8], bool active, int lane, int64_t cu,
+                                                   int64_t col, int64_t o, int64_t words_per_row,
+                                                   int64_t groups_per_row, uint32_t* __restrict__ codes,
+                                                   uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    constexpr int GL = GROUP / 8;                 // lanes per group
+    // Group range (NaN ignored: v_min/v_max return the non-NaN operand).
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+#pragma unroll
+    for (int m = 1; m < GL; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m));
+        mx = fmaxf(mx, __shfl_xor(mx, m));
+    }
+    mn = fminf(0.0f, mn);
+    mx = fmaxf(0.0f, mx);
+    const float d32 = (mx - mn) / QMAX;
+    const uint16_t dh = d32 == 0.0f ? (uint16_t)0x3C00 : f32_to_f16_up(d32);
+    const float df = f16_to_f32(dh);
+    const float z = fminf(fmaxf(rintf((-mn) / df), 0.0f), QMAX);
+    const float inv = 1.0f / df;
+
+    uint64_t field = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float q = fminf(fmaxf(rintf(v[i] * inv) + z, 0.0f), QMAX);
+        q = (v[i] != v[i]) ? 0.0f : q;
+        field |= (uint64_t)(uint32_t)q << (BITS * i);
+    }
+
+    // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words.
+    const int qbase = lane & ~3;
+    uint64_t fq[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint64_t lo = (uint32_t)__shfl((int)(uint32_t)field, qbase + k);
+        uint64_t hi = 0;
+        if constexpr (BITS * 8 > 32) hi = (uint32_t)__shfl((int)(uint32_t)(field >> 32), qbase + k);
+        fq[k] = lo | (hi << 32);
+    }
+    auto word = [&](int j) -> uint32_t {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int off = 8 * BITS * k - 32 * j;
+            if (off >= 32 || off + 8 * BITS <= 0) continue;
+            wv |= off >= 0 ? (uint32_t)(fq[k] << off) : (uint32_t)(fq[k] >> (-off));
+        }
+        return wv;
+    };
+    if (active) {
+        const int j = lane & 3;
+        uint32_t* wrow = codes + o * words_per_row + (cu >> 2) * BITS;
+        if (j < BITS) wrow[j] = word(j);
+        if (BITS > 4 && j == 0) wrow[4] = word(4);
+        if ((cu % GL) == 0) {
+            const int64_t gi = o * groups_per_row + col / GROUP;
+            scale[gi] = dh;
+            zero[gi] = f32_to_f16_rne(z);
+        }
+    }
+}
+
 template <int BITS, int GROUP, bool WF32, bool LOWRANK>
 __global__ __launch_bounds__(kQThreads) void k_quantize(
     const void* __restrict__ W, int64_t M, int64_t K, int64_t ldw, const float* __restrict__ s,
     const float* __restrict__ B, const float* __restrict__ A, int rank, int rows_per_block,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
-    constexpr float QMAX = (float)((1 << BITS) - 1);
-    constexpr int GL = GROUP / 8;                 // lanes per group
     extern __shared__ float sA[];                 // [rank][kQChans] when LOWRANK
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -57,24 +122,41 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const int64_t words_per_row = K * BITS / 32;
     const int64_t groups_per_row = K / GROUP;
 
-    for (int64_t o = row0 + wave; o < row1; o += kQThreads / kWave) {
-        float v[8];
-        if (active) {
-            float w[8];
-            if constexpr (WF32) {
-                const f32x4* p = (const f32x4*)((const float*)W + o * ldw + col);
-                f32x4 a = ld_nc(p), b = ld_nc(p + 1);
+    constexpr int RB = 4;                         // rows per wave whose loads are in flight together
+    constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
+    for (int64_t ob = row0 + wave; ob < row1; ob += WSTRIDE * RB) {
+        float wbuf[RB][8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { w[i] = a[i]; w[4 + i] = b[i]; }
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (active && o < row1) {
+                if constexpr (WF32) {
+                    const f32x4* p = (const f32x4*)((const float*)W + o * ldw + col);
+                    f32x4 a = ld_nc(p), b = ld_nc(p + 1);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { wbuf[r][i] = a[i]; wbuf[r][4 + i] = b[i]; }
+                } else {
+                    u32x4 p = ld_nc((const u32x4*)((const uint16_t*)W + o * ldw + col));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        wbuf[r][2 * i] = bf16lo_to_f32(p[i]);
+                        wbuf[r][2 * i + 1] = bf16hi_to_f32(p[i]);
+                    }
+                }
             } else {
-                u32x4 p = ld_nc((const u32x4*)((const uint16_t*)W + o * ldw + col));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { w[2 * i] = bf16lo_to_f32(p[i]); w[2 * i + 1] = bf16hi_to_f32(p[i]); }
+                for (int i = 0; i < 8; ++i) wbuf[r][i] = 0.0f;
             }
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (o >= row1) break;                 // wave-uniform
+            float v[8];
             if constexpr (LOWRANK) {
                 double acc[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = (double)w[i];
+                for (int i = 0; i < 8; ++i) acc[i] = (double)wbuf[r][i];
                 const float* Brow = B + o * rank;
                 for (int k = 0; k < rank; ++k) {
                     const double nb = -(double)Brow[k];
@@ -90,68 +172,10 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
                 for (int i = 0; i < 8; ++i) v[i] = (float)(acc[i] * (double)sc[i]);
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = w[i] * sc[i];
+                for (int i = 0; i < 8; ++i) v[i] = wbuf[r][i] * sc[i];
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-        }
-
-        // Group range (NaN ignored: v_min/v_max return the non-NaN operand).
-        float mn = v[0], mx = v[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-#pragma unroll
-        for (int m = 1; m < GL; m <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, m));
-            mx = fmaxf(mx, __shfl_xor(mx, m));
-        }
-        mn = fminf(0.0f, mn);
-        mx = fmaxf(0.0f, mx);
-        const float d32 = (mx - mn) / QMAX;
-        const uint16_t dh = d32 == 0.0f ? (uint16_t)0x3C00 : f32_to_f16_up(d32);
-        const float df = f16_to_f32(dh);
-        const float z = fminf(fmaxf(rintf((-mn) / df), 0.0f), QMAX);
-        const float inv = 1.0f / df;
-
-        uint64_t field = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float q = fminf(fmaxf(rintf(v[i] * inv) + z, 0.0f), QMAX);
-            q = (v[i] != v[i]) ? 0.0f : q;
-            field |= (uint64_t)(uint32_t)q << (BITS * i);
-        }
-
-        // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words.
-        const int qbase = lane & ~3;
-        uint64_t fq[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint64_t lo = (uint32_t)__shfl((int)(uint32_t)field, qbase + k);
-            uint64_t hi = 0;
-            if constexpr (BITS * 8 > 32) hi = (uint32_t)__shfl((int)(uint32_t)(field >> 32), qbase + k);
-            fq[k] = lo | (hi << 32);
-        }
-        auto word = [&](int j) -> uint32_t {
-            uint32_t wv = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int off = 8 * BITS * k - 32 * j;
-                if (off >= 32 || off + 8 * BITS <= 0) continue;
-                wv |= off >= 0 ? (uint32_t)(fq[k] << off) : (uint32_t)(fq[k] >> (-off));
-            }
-            return wv;
-        };
-        if (active) {
-            const int j = lane & 3;
-            uint32_t* wrow = codes + o * words_per_row + (cu >> 2) * BITS;
-            if (j < BITS) wrow[j] = word(j);
-            if (BITS > 4 && j == 0) wrow[4] = word(4);
-            if ((cu % GL) == 0) {
-                const int64_t gi = o * groups_per_row + col / GROUP;
-                scale[gi] = dh;
-                zero[gi] = f32_to_f16_rne(z);
-            }
+            quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
+                                            codes, scale, zero);
         }
     }
 }

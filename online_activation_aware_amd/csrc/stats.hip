@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     if (c0 < K) {
         if constexpr (XF32) {
             const float* base = (const float*)X + c0;
-#pragma unroll 4
+#pragma unroll 8
             for (int64_t t = t0 + wave; t < t1; t += 4) {
                 const f32x4* p = (const f32x4*)(base + t * ldx);
                 f32x4 a = ld_nc(p), b = ld_nc(p + 1);
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
             }
         } else {
             const uint16_t* base = (const uint16_t*)X + c0;
-#pragma unroll 4
+#pragma unroll 8
             for (int64_t t = t0 + wave; t < t1; t += 4) {
                 u32x4 w = ld_nc((const u32x4*)(base + t * ldx));
 #pragma unroll
@@ -83,19 +83,35 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     }
 }
 
+// Sum of the chunk partials: a workgroup covers 64 channels; its four waves
+// take every fourth chunk and the four sums are added in wave order.
 __global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ part, int nchunks,
                                                      int64_t K, double* __restrict__ ssq,
                                                      int accumulate) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= K) return;
+    __shared__ double red[4][64];
+    const int c = threadIdx.x & 63, p = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + c;
     double s = 0.0;
-    for (int c = 0; c < nchunks; ++c) s += part[(int64_t)c * K + j];
-    ssq[j] = accumulate ? ssq[j] + s : s;
+    if (j < K) {
+#pragma unroll 4
+        for (int ch = p; ch < nchunks; ch += 4) s += part[(int64_t)ch * K + j];
+    }
+    red[p][c] = s;
+    __syncthreads();
+    if (p == 0 && j < K) {
+        double tot = red[0][c];
+        tot += red[1][c];
+        tot += red[2][c];
+        tot += red[3][c];
+        ssq[j] = accumulate ? ssq[j] + tot : tot;
+    }
 }
 
 // [TTQ §method b2-b4]: c = ssq / T; lambda = lambda_rel * mean(c);
 // s = (c + lambda)^(alpha/2) in fp64, rounded once to fp32; 1 where c+lambda == 0.
-constexpr int kScaleThreads = 1024;
+// Every workgroup forms the same mean(c) (same fixed summation order), then
+// the scales of its own 256 channels.
+constexpr int kScaleThreads = 256;
 
 __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __restrict__ ssq,
                                                               int64_t n_tokens, int64_t K,
@@ -114,29 +130,25 @@ __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __re
     }
     const double lam = lambda_rel * (red[0] / (double)K);
     const double e = alpha / 2.0;
-    for (int64_t j = tid; j < K; j += kScaleThreads) {
+    const int64_t j = (int64_t)blockIdx.x * kScaleThreads + tid;
+    if (j < K) {
         const double cl = ssq[j] / tn + lam;
         s[j] = cl == 0.0 ? 1.0f : (float)pow(cl, e);
     }
 }
 
-__global__ __launch_bounds__(256) void k_inv_scales(const float* __restrict__ s, int64_t K,
-                                                    float* __restrict__ inv) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j < K) inv[j] = s ? 1.0f / s[j] : 1.0f;
-}
-
 // ------------------------------------------------------------------ host
 
 int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk) {
-    // Aim for >= ~1024 workgroups while keeping each chunk >= 16 rows, so the
-    // fp64 partials stay a small fraction of the bytes read.
+    // At most 32 token chunks (the fp64 partials stay <= 32 K doubles, a small
+    // fraction of the bytes read), at least ~1024 workgroups where T allows,
+    // and whole multiples of the 4 waves' row stride.
     const int64_t strips = (K + kStatsChans - 1) / kStatsChans;
-    int64_t want_chunks = (1024 + strips - 1) / strips;
-    int64_t rows = (T + want_chunks - 1) / want_chunks;
-    if (rows < 16) rows = 16;
+    int64_t want = (1024 + strips - 1) / strips;
+    if (want > 32) want = 32;
+    if (want < 1) want = 1;
+    int64_t rows = (T + want - 1) / want;
     rows = (rows + 3) / 4 * 4;
-    if (rows > T && T > 0) rows = (T + 3) / 4 * 4;
     if (rows <= 0) rows = 4;
     *rows_per_chunk = (int)rows;
     return T > 0 ? (int)((T + rows - 1) / rows) : 0;
@@ -153,18 +165,14 @@ hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t 
         else
             k_stats_partial<false><<<grid, kStatsThreads, 0, st>>>(X, T, K, ldx, rows, part);
     }
-    k_stats_final<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(part, nchunks, K, ssq, accumulate);
+    k_stats_final<<<(unsigned)((K + 63) / 64), 256, 0, st>>>(part, nchunks, K, ssq, accumulate);
     return hipGetLastError();
 }
 
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float* s, hipStream_t st) {
-    k_awq_scales<<<1, kScaleThreads, 0, st>>>(ssq, n_tokens, K, (double)alpha, (double)lambda_rel, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_inv_scales(const float* s, int64_t K, float* inv, hipStream_t st) {
-    k_inv_scales<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(s, K, inv);
+    k_awq_scales<<<(unsigned)((K + kScaleThreads - 1) / kScaleThreads), kScaleThreads, 0, st>>>(
+        ssq, n_tokens, K, (double)alpha, (double)lambda_rel, s);
     return hipGetLastError();
 }
 

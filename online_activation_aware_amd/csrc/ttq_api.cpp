@@ -109,12 +109,14 @@ ttq_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
     return TTQ_OK;
 }
 
+// The statistics use at most kMaxStatsChunks token chunks whatever T is, so
+// one workspace fits every prompt length.
+constexpr int kMaxStatsChunks = 32;
 size_t ws_stats(int64_t T, int64_t K) {
-    int rows = 0;
-    const int nch = ttq::stats_chunks(T, K, &rows);
-    return round_up((size_t)nch * (size_t)K * sizeof(double));
+    if (T <= 0) return 0;
+    return round_up((size_t)kMaxStatsChunks * (size_t)K * sizeof(double));
 }
-size_t ws_qgemm(int64_t K) { return round_up((size_t)K * sizeof(float)); }
+size_t ws_qgemm(int64_t K) { (void)K; return 0; }
 size_t ws_lowrank(int64_t T, int64_t K, int rank) {
     if (rank <= 0 || T <= 0) return 0;
     int64_t len = 0;
@@ -223,10 +225,8 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, c
     if (T == 0 || M == 0) return TTQ_OK;
     if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
     if (ttq_status e = check_ws(ws, ws_bytes, ws_qgemm(K))) return e;
-    float* inv = (float*)ws;
     hipStream_t st = as_stream(stream);
-    if (ttq_status e = device_status(ttq::launch_inv_scales(s, K, inv, st), "ttq_qgemm launch")) return e;
-    return device_status(ttq::launch_qgemm(X, xt == TTQ_F32, T, K, ldx, inv, (const uint32_t*)codes,
+    return device_status(ttq::launch_qgemm(X, xt == TTQ_F32, T, K, ldx, s, (const uint32_t*)codes,
                                            scale_f16, zero_f16, M, bits, group, Y, yt == TTQ_F32, ldy, st),
                          "ttq_qgemm launch");
 }
@@ -291,10 +291,8 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                                  a->A, a->rank, (uint32_t*)codes, scale, zero, st),
             "quantize"))
         return e;
-    float* inv = (float*)scratch;
-    if (ttq_status e = device_status(ttq::launch_inv_scales(s, a->K, inv, st), "inv_scales")) return e;
     if (ttq_status e = device_status(
-            ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, inv, (const uint32_t*)codes, scale, zero,
+            ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero,
                               a->M, a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, st),
             "qgemm"))
         return e;

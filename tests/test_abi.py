@@ -127,8 +127,8 @@ def test_qgemm_rejects(L):
     assert call(Y=FAKE + 2) == 1                        # fp32 Y not 4-byte aligned
     assert call(ldx=260) == 1                           # X rows (520 B) not a multiple of 16 bytes
     assert call(s=None) == 1
-    assert call(ws=None) == 1
-    assert call(wsb=16) == 1
+    assert call(codes=FAKE + 4) == 1                    # codes not 16-byte aligned
+    assert call(bits=1) == 1
     assert call(yt=7) == 1
     assert call(T=0) == 0 and call(M=0) == 0            # empty calls
 
