@@ -354,21 +354,23 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 }
 
 constexpr int kWThreads = 512;                   // 8 waves: two per SIMD
+constexpr int kWMath = 4;                        // waves 0..3: MFMA; 4..7: producers
 
 // Requires K % 64 == 0 and 256 rows of X addressable with 32-bit offsets.
 //
-// 128 rows x 256 tokens per workgroup of 8 waves (2 x 4, each 64 x 64:
-// 4 x 4 MFMA tiles of 16x16x32), two waves per SIMD so that one wave's
-// MFMAs overlap the other's LDS traffic and dequantization.  All global
-// data arrives by buffer->LDS DMA (no staging registers, few memory
-// instructions per step):
+// 128 rows x 256 tokens per workgroup, 8 waves with split roles so that on
+// every SIMD the matrix unit and the vector ALU work at the same time:
+//   math waves 0..3 (one per SIMD): 2 x 2 tiles of 64 rows x 128 tokens,
+//     4 x 8 MFMA 16x16x32 per 32-deep slice; they only read LDS;
+//   producer waves 4..7: issue every DMA and dequantize the weights.
+// All global data arrives by buffer->LDS DMA (few memory instructions):
 //   X     : 3-slot ring, step kt+2 issued during step kt;
 //   side  : codes, steps, zeros and s of a step, 3-slot ring, step kt+3
 //           issued during step kt (it is consumed one step early);
-//   W~    : step kt+1 dequantized from its side slot while step kt's MFMAs
-//           run, written to the other slot of a 2-slot ring.
-// One barrier per 64-deep K step; each wave waits only for its own DMA of
-// the data the next step needs.
+//   W~    : step kt+1 dequantized while step kt's MFMAs run, written to the
+//           other slot of a 2-slot ring.
+// One barrier per 64-deep K step; each producer wave waits only for its own
+// DMA of the data the next step needs.
 template <int BITS, int GROUP, bool YF32>
 __global__ __launch_bounds__(kWThreads, 1) void k_qgemm_wide(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
@@ -376,9 +378,11 @@ __global__ __launch_bounds__(kWThreads, 1) void k_qgemm_wide(
     const uint16_t* __restrict__ zero, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec) {
     using SL = SideLayout<BITS, GROUP>;
     constexpr bool STRADDLE = (8 * BITS) % 32 != 0 && BITS != 2;
-    constexpr int XDMA = kWBN * kWRowB / 1024 / (kWThreads / kWave);  // 1 KB X DMA ops per wave (4)
-    constexpr int NWAVE = kWThreads / kWave;
-    constexpr int UNITS = kWBM * kWBK / 8 / kWThreads;                // 8-code units per thread (2)
+    constexpr int NPROD = kWThreads / kWave - kWMath;                 // producer waves (4)
+    constexpr int XDMA = kWBN * kWRowB / 1024 / NPROD;                // 1 KB X DMA ops per producer (8)
+    constexpr int PTHREADS = NPROD * kWave;                            // 256
+    constexpr int UNITS = kWBM * kWBK / 8 / PTHREADS;                  // 8-code units per producer thread (4)
+    constexpr int RSTRIDE = PTHREADS / 8;                              // 32
     __shared__ __attribute__((aligned(1024))) uint8_t sX0[kWBN * kWRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sX1[kWBN * kWRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sX2[kWBN * kWRowB];
@@ -391,7 +395,10 @@ __global__ __launch_bounds__(kWThreads, 1) void k_qgemm_wide(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 2, wn = wave & 3;
+    const bool math = wave < kWMath;
+    const int wm = wave >> 1, wn = wave & 1;      // math tile (valid for math waves)
+    const int pw = wave - kWMath;                 // producer index (valid for producers)
+    const int ptid = tid - kWMath * kWave;
     const int64_t o0 = (int64_t)blockIdx.x * kWBM;
     const int64_t t0 = (int64_t)blockIdx.y * kWBN;
     const int rows_x = (int)min((int64_t)kWBN, T - t0);
@@ -410,40 +417,40 @@ __global__ __launch_bounds__(kWThreads, 1) void k_qgemm_wide(
     const rsrc_t rzz = make_rsrc((const uint8_t*)zero + o0 * gprb, szb);
     const rsrc_t rs = make_rsrc(s, K * 4);
 
-    // X DMA: wave w, op i fills LDS rows 8(XDMA w + i) .. +7; lane l lands in
-    // row 8(XDMA w + i) + l/8 at chunk position l%8, which holds chunk (l%8)^(row&7).
+    // X DMA (producer pw, op i): fills LDS rows 8(XDMA pw + i) .. +7; lane l
+    // lands in row 8(XDMA pw + i) + l/8 at chunk position l%8, which holds
+    // chunk (l%8)^(row&7).
     const int xrow_l = lane >> 3;
     const int xchunk = (lane & 7) ^ xrow_l;
-    const int xoff0 = ((wave * 8 * XDMA + xrow_l) * (int)ldx + 8 * xchunk) * 2;
+    const int xoff0 = ((pw * 8 * XDMA + xrow_l) * (int)ldx + 8 * xchunk) * 2;
     const int xrow8 = 8 * (int)ldx * 2;           // byte distance of 8 token rows
 
-    // Side DMA: ops q = wave, wave + 8, ... of SL::NS; this wave issues my_side of them.
-    const int my_side = wave < SL::NS ? (SL::NS - wave + NWAVE - 1) / NWAVE : 0;
+    // Side DMA: ops q = pw, pw + NPROD, ... of SL::NS.
+    const int my_side = (!math && pw < SL::NS) ? (SL::NS - pw + NPROD - 1) / NPROD : 0;
 
-    // Dequant role: unit cu = tid % 8 (8 columns) of rows rsub + 64 i.
-    constexpr int RSTRIDE = kWThreads / 8;        // 64
-    const int cu = tid & 7;
-    const int rsub = tid >> 3;
+    // Dequant role: unit cu = ptid % 8 (8 columns) of rows rsub + 32 i.
+    const int cu = ptid & 7;
+    const int rsub = ptid >> 3;
     const int ubit = 8 * cu * BITS;               // bit offset of the unit in its row's step segment
     const int ushift = ubit & 31;
     const int gi = GROUP <= 64 ? (8 * cu) / GROUP : 0;
-    const int wdst = swz(rsub, cu);               // + RSTRIDE i rows (same swizzle: 64 i % 8 == 0)
+    const int wdst = swz(rsub, cu);               // + RSTRIDE i rows (same swizzle: 32 i % 8 == 0)
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto issue_x = [&](uint8_t* dst, int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < XDMA; ++i)
-            dma_to_lds<16>(rx, dst + (wave * XDMA + i) * 1024, xoff0 + i * xrow8, (int)k0 * 2);
+            dma_to_lds<16>(rx, dst + (pw * XDMA + i) * 1024, xoff0 + i * xrow8, (int)k0 * 2);
     };
     auto issue_side = [&](uint8_t* dst, int64_t k0) __attribute__((always_inline)) {
         const int kc = (int)(k0 * BITS / 8);      // byte offset of the step in a code row
         const int kg = (int)(k0 / GROUP) * 2;
-        for (int q = wave; q < SL::NS; q += NWAVE) {
+        for (int q = pw; q < SL::NS; q += NPROD) {
             if (q < SL::C) {
                 const int li = q * kWave + lane, r = li / SL::CL, sg = li % SL::CL;
                 dma_to_lds<SL::CLS>(rc, dst + SL::OFF_C + q * kWave * SL::CLS, r * wprb + sg * SL::CLS, kc);
@@ -501,99 +508,93 @@ __global__ __launch_bounds__(kWThreads, 1) void k_qgemm_wide(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int c = 4 * kk + (lane >> 4);
-            u32x4 a[4], b[4];
+            u32x4 a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(ws + swz(wm * 64 + 16 * i + (lane & 15), c));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = *(const u32x4*)(xs + swz(wn * 64 + 16 * j + (lane & 15), c));
+            for (int jh = 0; jh < 2; ++jh) {
+                u32x4 b[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j)
+                    b[j] = *(const u32x4*)(xs + swz(wn * 128 + 64 * jh + 16 * j + (lane & 15), c));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][4 * jh + j] = mfma_16x16x32(a[i], b[j], acc[i][4 * jh + j]);
+            }
         }
     };
 
     // Step kt with static slots: xc/xn = X slots of kt / kt+2, wc/wn_ = W~
     // slots of kt / kt+1, s1 = side slot of kt+1 (dequantized now), s3 = side
-    // slot for kt+3 (issued now).  Flags: SIDE = step kt+3 exists, XN = step
-    // kt+2 exists, NEXT = step kt+1 exists.
-    auto step = [&](auto SIDE, auto XN, auto NEXT, uint8_t* xc, uint8_t* xn, uint8_t* wc, uint8_t* wn_,
+    // slot for kt+3 (issued now); side/xnext/next: steps kt+3 / kt+2 / kt+1 exist.
+    auto step = [&](bool side, bool xnext, bool next, uint8_t* xc, uint8_t* xn, uint8_t* wc, uint8_t* wn_,
                     const uint8_t* s1, uint8_t* s3, int64_t kt) __attribute__((always_inline)) {
-        if constexpr (decltype(SIDE)::value) issue_side(s3, (kt + 3) * kWBK);
-        if constexpr (decltype(XN)::value) issue_x(xn, (kt + 2) * kWBK);
-        __builtin_amdgcn_sched_barrier(0);        // keep the prefetch ahead of this step's work
-        compute(xc, wc);
-        if constexpr (decltype(NEXT)::value) dequant_store(s1, wn_, (kt + 1) * kWBK);
-        // The DMA issued during this step may stay in flight; all older DMA
-        // (step kt+1's X, step kt+2's side data) must have landed.
-        wait_vmcnt_rt((decltype(SIDE)::value ? my_side : 0) + (decltype(XN)::value ? XDMA : 0));
-        sync_lds();
-    };
-    using Y_ = std::true_type;
-    using N_ = std::false_type;
-    // The last steps: one body with runtime flags (same static slots).
-    auto step_rt = [&](uint8_t* xc, uint8_t* xn, uint8_t* wc, uint8_t* wn_, const uint8_t* s1, uint8_t* s3,
-                       int64_t kt, int64_t nk) __attribute__((always_inline)) {
-        const bool side = kt + 3 < nk, xnext = kt + 2 < nk;
-        if (side) issue_side(s3, (kt + 3) * kWBK);
-        if (xnext) issue_x(xn, (kt + 2) * kWBK);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(xc, wc);
-        if (kt + 1 < nk) dequant_store(s1, wn_, (kt + 1) * kWBK);
-        wait_vmcnt_rt((side ? my_side : 0) + (xnext ? XDMA : 0));
+        if (math) {
+            compute(xc, wc);
+        } else {
+            if (side) issue_side(s3, (kt + 3) * kWBK);
+            if (xnext) issue_x(xn, (kt + 2) * kWBK);
+            if (next) dequant_store(s1, wn_, (kt + 1) * kWBK);
+            // The DMA issued during this step may stay in flight; all older
+            // DMA (step kt+1's X, step kt+2's side data) must have landed.
+            wait_vmcnt_rt((side ? my_side : 0) + (xnext ? XDMA : 0));
+        }
         sync_lds();
     };
 
     const int64_t nk = K / kWBK;
-    // Prologue: side 0, X 0, side 1, X 1, side 2; dequantize step 0.
-    issue_side(sS0, 0);
-    issue_x(sX0, 0);
-    int pending = 0;                              // DMA ops allowed to remain in flight
-    if (nk > 1) {
-        issue_side(sS1, kWBK);
-        issue_x(sX1, kWBK);
-        pending = XDMA;
-    }
-    if (nk > 2) {
-        issue_side(sS2, 2 * kWBK);
-        pending += my_side;
-    }
-    if (nk > 1) {
-        // side 0 and X 0 must be in LDS; side 1 is needed by step 0's dequant.
-        wait_vmcnt_rt(pending);
-    } else {
-        wait_vmcnt<0>();
+    // Prologue (producers): side 0, X 0, side 1, X 1, side 2; dequantize step 0.
+    if (!math) {
+        issue_side(sS0, 0);
+        issue_x(sX0, 0);
+        int pending = 0;                          // DMA ops allowed to remain in flight
+        if (nk > 1) {
+            issue_side(sS1, kWBK);
+            issue_x(sX1, kWBK);
+            pending = XDMA;
+        }
+        if (nk > 2) {
+            issue_side(sS2, 2 * kWBK);
+            pending += my_side;
+        }
+        wait_vmcnt_rt(nk > 1 ? pending : 0);      // side 0, X 0 and side 1 have landed
     }
     sync_lds();
-    dequant_store(sS0, sW0, 0);
+    if (!math) dequant_store(sS0, sW0, 0);
     sync_lds();
 
     // Slot sequence (period 6): X slot kt%3, W~ slot kt%2, side slot kt%3.
     int64_t kt = 0;
     for (; kt + 9 <= nk; kt += 6) {
-        step(Y_{}, Y_{}, Y_{}, sX0, sX2, sW0, sW1, sS1, sS0, kt + 0);
-        step(Y_{}, Y_{}, Y_{}, sX1, sX0, sW1, sW0, sS2, sS1, kt + 1);
-        step(Y_{}, Y_{}, Y_{}, sX2, sX1, sW0, sW1, sS0, sS2, kt + 2);
-        step(Y_{}, Y_{}, Y_{}, sX0, sX2, sW1, sW0, sS1, sS0, kt + 3);
-        step(Y_{}, Y_{}, Y_{}, sX1, sX0, sW0, sW1, sS2, sS1, kt + 4);
-        step(Y_{}, Y_{}, Y_{}, sX2, sX1, sW1, sW0, sS0, sS2, kt + 5);
+        step(true, true, true, sX0, sX2, sW0, sW1, sS1, sS0, kt + 0);
+        step(true, true, true, sX1, sX0, sW1, sW0, sS2, sS1, kt + 1);
+        step(true, true, true, sX2, sX1, sW0, sW1, sS0, sS2, kt + 2);
+        step(true, true, true, sX0, sX2, sW1, sW0, sS1, sS0, kt + 3);
+        step(true, true, true, sX1, sX0, sW0, sW1, sS2, sS1, kt + 4);
+        step(true, true, true, sX2, sX1, sW1, sW0, sS0, sS2, kt + 5);
     }
     for (; kt < nk; kt += 6) {
-        step_rt(sX0, sX2, sW0, sW1, sS1, sS0, kt + 0, nk);
-        if (kt + 1 < nk) step_rt(sX1, sX0, sW1, sW0, sS2, sS1, kt + 1, nk);
-        if (kt + 2 < nk) step_rt(sX2, sX1, sW0, sW1, sS0, sS2, kt + 2, nk);
-        if (kt + 3 < nk) step_rt(sX0, sX2, sW1, sW0, sS1, sS0, kt + 3, nk);
-        if (kt + 4 < nk) step_rt(sX1, sX0, sW0, sW1, sS2, sS1, kt + 4, nk);
-        if (kt + 5 < nk) step_rt(sX2, sX1, sW1, sW0, sS0, sS2, kt + 5, nk);
+#define TTQ_TAIL(J, XC, XN, WC, WN, S1, S3)                                                             \
+        if (kt + J < nk)                                                                                \
+            step(kt + J + 3 < nk, kt + J + 2 < nk, kt + J + 1 < nk, XC, XN, WC, WN, S1, S3, kt + J)
+        TTQ_TAIL(0, sX0, sX2, sW0, sW1, sS1, sS0);
+        TTQ_TAIL(1, sX1, sX0, sW1, sW0, sS2, sS1);
+        TTQ_TAIL(2, sX2, sX1, sW0, sW1, sS0, sS2);
+        TTQ_TAIL(3, sX0, sX2, sW1, sW0, sS1, sS0);
+        TTQ_TAIL(4, sX1, sX0, sW0, sW1, sS2, sS1);
+        TTQ_TAIL(5, sX2, sX1, sW1, sW0, sS0, sS2);
+#undef TTQ_TAIL
     }
 
+    if (!math) return;
     // Epilogue: lane holds Y^T[o + r][t] for r = 0..3 (4 consecutive o of token t).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t o = o0 + wm * 64 + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + wn * 64 + 16 * j + (lane & 15);
+        for (int j = 0; j < 8; ++j) {
+            const int64_t t = t0 + wn * 128 + 16 * j + (lane & 15);
             if (t >= T) continue;
             if constexpr (YF32) {
                 float* yp = (float*)Y + t * ldy + o;
