@@ -11,8 +11,9 @@ Inputs rotate over several copies (>= 768 MiB in total) so that successive
 steps do not find X and W in the 256 MiB Infinity Cache.
 
 Prints one JSON line (stdout): the layer time in microseconds, the roofline
-of the dominant kernel (the quantized GEMM) from HIP events on the launch
-stream, the per-stage breakdown, and the CPU oracle timed on the host.
+of the dominant kernel (the projection GEMM) from HIP events that ttq_linear
+records on its stream in every timed step, the per-stage breakdown, and the
+CPU oracle timed on the host.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -33,7 +34,7 @@ METRIC = "ttq_linear µs/layer (stats+quant+qGEMM); qGEMM TFLOP/s; HBM GB/s vs p
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 
-# HBM bytes per qGEMM launch measured with rocprofv3 --pmc (FETCH_SIZE and
+# HBM bytes per projection-GEMM launch measured with rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE, scaled by the factor a plain copy of known size gives), keyed by
 # the SHA-256 of the kernel source they were taken on.  A source change
 # invalidates them (traffic is then reported as null).
@@ -45,7 +46,7 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    path = os.path.join(ROOT, "online_activation_aware_amd", "csrc", "qgemm.hip")
+    path = os.path.join(ROOT, "online_activation_aware_amd", "csrc", "gemm_bf16.hip")
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -55,16 +56,18 @@ def esize(dt: str) -> int:
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Bytes each kernel must move at minimum (Y in fp32)."""
+    """Bytes each stage must move at minimum (Y in fp32): statistics read X
+    and write ssq; the quantizer reads W (and the factors) and ssq, writes s,
+    codes, steps and zeros; the projection reads X, codes, steps, zeros and s
+    and writes Y."""
     T, K, M, b, g = wl.T, wl.K, wl.M, wl.bits, wl.group
     codes = M * K * b // 8
     steps = 2 * M * (K // g) * 2
     return {
         "stats": T * K * esize(wl.xdtype) + K * 8,
-        "scales": K * 8 + K * 4,
-        "quantize": M * K * esize(wl.wdtype) + K * 4 + codes + steps
+        "quantize": M * K * esize(wl.wdtype) + K * 8 + K * 4 + codes + steps
         + (wl.rank * (M + K) * 4 if wl.rank else 0),
-        "qgemm": T * K * esize(wl.xdtype) + K * 4 + codes + steps + T * M * 4,
+        "projection": T * K * esize(wl.xdtype) + K * 4 + codes + steps + T * M * 4,
     }
 
 
@@ -97,7 +100,7 @@ def cpu_baseline(wl, data, B=None, A=None) -> dict:
         threads = 1
     times = []
     t_start = time.perf_counter()
-    while len(times) < 9 and (len(times) < 3 or time.perf_counter() - t_start < 10.0):
+    while len(times) < 64 and (len(times) < 3 or time.perf_counter() - t_start < 10.0):
         t0 = time.perf_counter()
         ssq = oracle.stats(data["X"], wl.xdtype)
         s = oracle.awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel)
@@ -184,15 +187,16 @@ def main(argv=None) -> int:
     ws = ttq.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, wl.rank, device=dev)
     Y = torch.empty((wl.T, wl.M), dtype=torch.float32, device=dev)
 
-    def step(i):
+    def step(i, events=None):
         ttq.ttq_linear(Xs[i % ncopy], Ws[i % ncopy], wl.bits, wl.group, wl.alpha, wl.lambda_rel,
-                       B=B, A=A, Y=Y, ws=ws, state=st)
+                       B=B, A=A, Y=Y, ws=ws, state=st, stage_events=events)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # Timed region: K steps back to back, nothing else on the stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -205,52 +209,49 @@ def main(argv=None) -> int:
     ms = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/layer (wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
 
-    # Per-stage breakdown: the same kernels through the individual entry points,
-    # each bracketed by events on the launch stream.
-    stages = ["stats", "scales", "quantize", "qgemm"] + (["lowrank"] if wl.rank else [])
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        X, W = Xs[i % ncopy], Ws[i % ncopy]
-        ev = evs[i]
-        ev[0].record()
-        ttq.ttq_stats(X, st["ssq"], ws=ws)
-        ev[1].record()
-        ttq.ttq_awq_scales(st["ssq"], wl.T, wl.alpha, wl.lambda_rel, s=st["s"])
-        ev[2].record()
-        ttq.ttq_quantize_groups(W, st["s"], wl.bits, wl.group, B=B, A=A, codes=st["codes"],
-                                scale_f16=st["scale_f16"], zero_f16=st["zero_f16"])
-        ev[3].record()
-        ttq.ttq_qgemm(X, st["s"], st["codes"], st["scale_f16"], st["zero_f16"], wl.M, wl.bits, wl.group,
-                      Y=Y, ws=ws)
-        ev[4].record()
-        if wl.rank:
-            ttq.ttq_lowrank_add(X, A, B, Y, ws=ws)
-            ev[5].record()
+    # Instrumented region: K more steps in which ttq_linear stamps HIP events
+    # with its own kernels' start and end times on the launch stream
+    # (hipExtLaunchKernel), one (start, stop) pair per stage.  The stamps cost
+    # a few microseconds of launch latency per kernel, so this region is not
+    # the one `value` comes from; the kernel durations themselves are exact.
+    evs = [ttq.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j, name in enumerate(stages)}
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per_step = [e.stage_ms() for e in evs]
+    stage_ms = {k: sum(p[k] for p in per_step) / args.steps for k in ttq.LINEAR_STAGES}
+    if not wl.rank:
+        stage_ms.pop("lowrank")
+
     alg = algorithmic_bytes(wl)
     flops = 2.0 * wl.T * wl.M * wl.K
-    q_s = stage_ms["qgemm"] * 1e-3
-    achieved = flops / q_s / 1e12
+    proj_us = stage_ms["projection"] * 1e3
+    achieved = flops / (proj_us * 1e-6) / 1e12
     h = kernel_source_hash()
     traffic = MEASURED_TRAFFIC.get(h)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "k_qgemm (dequantize codes into LDS -> bf16 MFMA 16x16x32, fp32 accumulate)",
-                "flops_per_launch": flops, "avg_launch_us": round(stage_ms["qgemm"] * 1e3, 2)}
+                "kernel": "k_gemm_bf16 (Y = X W~^T on the dequantized weight; bf16 MFMA 16x16x32, "
+                          "fp32 accumulate, 128x256 tiles, buffer->LDS DMA)",
+                "flops_per_launch": flops, "avg_launch_us": round(proj_us, 2),
+                "timing": "kernel start/end stamped into HIP events by ttq_linear on its stream "
+                          f"(hipExtLaunchKernel), averaged over {args.steps} instrumented steps"}
     breakdown = {}
-    for name in stages:
-        us = stage_ms[name] * 1e3
+    for name, v in stage_ms.items():
+        us = v * 1e3
         d = {"us": round(us, 2)}
         if name in alg:
             d["alg_bytes"] = alg[name]
             d["gbs"] = round(alg[name] / (us * 1e-6) / 1e9, 1)
             d["hbm_frac"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        if name == "quantize":
+            d["staged_bytes"] = wl.M * wl.K * 2     # dequantized weight written for the projection
         breakdown[name] = d
-    breakdown["qgemm"]["tflops"] = round(achieved, 2)
+    breakdown["projection"]["tflops"] = round(achieved, 2)
     for name, d in breakdown.items():
-        log(f"  {name:9s} {d['us']:8.2f} us" + (f"  {d['gbs']:8.1f} GB/s" if "gbs" in d else ""))
+        log(f"  {name:10s} {d['us']:8.2f} us" + (f"  {d['gbs']:8.1f} GB/s" if "gbs" in d else "")
+            + (f"  {d['tflops']:8.1f} TFLOP/s" if "tflops" in d else ""))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -35,7 +35,8 @@
  *    strides a multiple of 16 bytes; Y aligned to its element size, any row
  *    stride >= M; s 16-byte aligned; ssq 8-byte aligned; workspace 256-byte
  *    aligned.
- *  - Limits: K a positive multiple of 32 (of 8 for ttq_stats); bits in
+ *  - Limits: K a positive multiple of 32 (of 8 for ttq_stats), at most 2^18;
+ *    T, M and row strides at most 2^30; bits in
  *    {2,3,4,5}; group in {16,32,64,128} dividing K; 0 <= rank <= 32.
  *    T == 0 or M == 0 is a valid empty call (nothing is launched, except
  *    that ttq_stats with accumulate == 0 still zeroes ssq).
@@ -130,7 +131,13 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  *   X: [T][K] (xt), s: [K], codes/scale/zero as produced by
  *   ttq_quantize_groups for (M, K, bits, group).  Y: [T][M] fp32 or bf16
  *   (yt), overwritten.  Y must not overlap any input.
- *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes.
+ *   Two execution paths give the same bf16 weights: for bf16 X with
+ *   T >= 192 and K a multiple of 64 the weight is dequantized once into ws
+ *   (M*K bf16) and multiplied by a matrix-core GEMM; otherwise codes are
+ *   dequantized tile by tile inside the GEMM kernel.
+ *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (M*K*2
+ *   rounded up to 256 when T >= 192, none otherwise); only read and written
+ *   by the kernels this call enqueues.
  */
 ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
                      const float* s, const int32_t* codes, const uint16_t* scale_f16,
@@ -167,7 +174,21 @@ size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group,
  * The optional outputs (ssq, s, codes, scale_f16, zero_f16) receive the
  * prompt's quantization state so that later decode steps can call ttq_qgemm
  * on it; when NULL they live in the workspace.
+ * Execution: statistics (the reduction also forms lambda), then one
+ * quantizer pass that evaluates s for its channels (same arithmetic as
+ * ttq_awq_scales), writes codes, steps and zeros, and for bf16 X with
+ * T >= 192 and K a multiple of 64 also the dequantized weight into ws, which
+ * the matrix-core GEMM then multiplies (otherwise the fused kernel of
+ * ttq_qgemm runs); then the low-rank term.
+ * stage_events: NULL, or TTQ_LINEAR_STAGE_EVENTS hipEvent_t handles created
+ * by the caller: a (start, stop) pair for each of the statistics, the
+ * quantizer, the projection and the low-rank term, in that order.  The
+ * stage's first kernel stamps `start` when it starts and its last kernel
+ * stamps `stop` when it ends (kernel timestamps: nothing extra is enqueued);
+ * a stage that launches nothing (the low-rank term when rank == 0) records
+ * both on `stream` as markers.  For per-stage timing; never blocks.
  */
+#define TTQ_LINEAR_STAGE_EVENTS 8
 typedef struct ttq_linear_args {
     const void* X;  int xt;  int64_t T;  int64_t K;  int64_t ldx;
     const void* W;  int wt;  int64_t M;  int64_t ldw;
@@ -176,6 +197,7 @@ typedef struct ttq_linear_args {
     const float* B;  const float* A;  int rank;
     void* Y;  int yt;  int64_t ldy;
     double* ssq;  float* s;  int32_t* codes;  uint16_t* scale_f16;  uint16_t* zero_f16;
+    void* const* stage_events;
 } ttq_linear_args;
 
 ttq_status ttq_linear(const ttq_linear_args* args, void* ws, size_t ws_bytes, void* stream);

@@ -1,0 +1,152 @@
+// Projection with an already dequantized (QDQ) weight: Y = X W~^T on the
+// gfx950 matrix cores, bf16 operands, fp32 accumulation.
+//
+// [TTQ §method b1] quantization with QDQ operations: for prompt-sized token
+// counts the weight is dequantized once, w~[o][j] = bf16((code - zero) * step
+// * (1/s[j])) (written by the quantizer, or by k_dequant from packed codes),
+// and every token tile then reuses it.  The per-element arithmetic is exactly
+// that of the fused dequantize-in-LDS kernel, so both paths see identical
+// bf16 weights.
+//
+// Tiling: 128 output rows x 256 tokens per workgroup, 8 waves (2 per SIMD),
+// each 64 x 64 (4 x 4 MFMA 16x16x32 per 32-deep slice).  Both operands arrive
+// by buffer->LDS DMA into 3-slot rings issued two steps ahead (no staging
+// registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
+// one barrier per 64-deep K step, each wave waiting only for its own DMA.
+#include "common.hpp"
+#include "launch.hpp"
+#include "lds_dma.hpp"
+
+namespace ttq {
+
+constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kBThreads = 512;
+constexpr int kBRowB = kBK * 2;                  // 128-byte LDS rows
+
+template <bool YF32>
+__global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const uint16_t* __restrict__ Wq,
+    int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec) {
+    constexpr int NW = kBThreads / kWave;                       // 8 waves
+    constexpr int XOPS = kBN * kBRowB / 1024 / NW;              // 1 KB DMA ops per wave for X (4)
+    constexpr int WOPS = kBM * kBRowB / 1024 / NW;              // ... for W~ (2)
+    constexpr int OPS = XOPS + WOPS;
+    __shared__ __attribute__((aligned(1024))) uint8_t sX0[kBN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX1[kBN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX2[kBN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[kBM * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW1[kBM * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW2[kBM * kBRowB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 2, wn = wave & 3;      // 2 x 4 waves of 64 x 64
+    const int64_t o0 = (int64_t)blockIdx.x * kBM;
+    const int64_t t0 = (int64_t)blockIdx.y * kBN;
+    const int rows_x = (int)min((int64_t)kBN, T - t0);
+    const int rows_w = (int)min((int64_t)kBM, M - o0);
+    const rsrc_t rx = make_rsrc(X + t0 * ldx, ((int64_t)(rows_x - 1) * ldx + K) * 2);
+    const rsrc_t rw = make_rsrc(Wq + o0 * ldw, ((int64_t)(rows_w - 1) * ldw + K) * 2);
+
+    // DMA op i of this wave fills LDS rows 8 (ops*wave + i) .. +7; lane l lands
+    // in row (.. + l/8) at chunk position l%8, holding chunk (l%8) ^ (row & 7).
+    const int rl = lane >> 3;
+    const int ch = (lane & 7) ^ rl;
+    const int xoff0 = ((wave * 8 * XOPS + rl) * (int)ldx + 8 * ch) * 2;
+    const int woff0 = ((wave * 8 * WOPS + rl) * (int)ldw + 8 * ch) * 2;
+    const int xrow8 = 8 * (int)ldx * 2, wrow8 = 8 * (int)ldw * 2;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](uint8_t* xd, uint8_t* wd, int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < XOPS; ++i)
+            dma_to_lds<16>(rx, xd + (wave * XOPS + i) * 1024, xoff0 + i * xrow8, (int)k0 * 2);
+#pragma unroll
+        for (int i = 0; i < WOPS; ++i)
+            dma_to_lds<16>(rw, wd + (wave * WOPS + i) * 1024, woff0 + i * wrow8, (int)k0 * 2);
+    };
+    auto compute = [&](const uint8_t* xs, const uint8_t* ws) __attribute__((always_inline)) {
+        u32x4 a[2][4], b[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = 4 * kk + (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[kk][i] = *(const u32x4*)(ws + lds_swz(wm * 64 + 16 * i + (lane & 15), c));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[kk][j] = *(const u32x4*)(xs + lds_swz(wn * 64 + 16 * j + (lane & 15), c));
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a[kk][i], b[kk][j], acc[i][j]);
+    };
+    auto step = [&](bool more, const uint8_t* xc, const uint8_t* wc, uint8_t* xn, uint8_t* wn_, int64_t kt)
+        __attribute__((always_inline)) {
+        if (more) issue(xn, wn_, (kt + 2) * kBK);
+        __builtin_amdgcn_sched_barrier(0);        // keep the prefetch ahead of this step's work
+        compute(xc, wc);
+        if (more) wait_vmcnt<OPS>();              // step kt+1's operands have landed
+        else wait_vmcnt<0>();
+        sync_lds();
+    };
+
+    const int64_t nk = K / kBK;
+    issue(sX0, sW0, 0);
+    if (nk > 1) {
+        issue(sX1, sW1, kBK);
+        wait_vmcnt<OPS>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    sync_lds();
+    int64_t kt = 0;
+    for (; kt + 5 <= nk; kt += 3) {
+        step(true, sX0, sW0, sX2, sW2, kt + 0);
+        step(true, sX1, sW1, sX0, sW0, kt + 1);
+        step(true, sX2, sW2, sX1, sW1, kt + 2);
+    }
+    for (; kt < nk; kt += 3) {
+        step(kt + 2 < nk, sX0, sW0, sX2, sW2, kt + 0);
+        if (kt + 1 < nk) step(kt + 3 < nk, sX1, sW1, sX0, sW0, kt + 1);
+        if (kt + 2 < nk) step(kt + 4 < nk, sX2, sW2, sX1, sW1, kt + 2);
+    }
+
+    // Lane holds Y^T[o + r][t] for r = 0..3 (4 consecutive o of token t).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t o = o0 + wm * 64 + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + wn * 64 + 16 * j + (lane & 15);
+            if (t >= T) continue;
+            store_y4<YF32>(Y, t * ldy + o, M - o, yvec, acc[i][j]);
+        }
+    }
+}
+
+bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw) {
+    return T > 0 && K % kBK == 0 && (int64_t)kBN * ldx * 2 < ((int64_t)1 << 31) &&
+           (int64_t)kBM * ldw * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
+                            int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
+                            StageTimer tm) {
+    const int yvec = ((uintptr_t)Y % 16 == 0) && ((ldy * (yf32 ? 4 : 2)) % 16 == 0);
+    dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((T + kBN - 1) / kBN));
+    if (yf32)
+        return launch_kernel(k_gemm_bf16<true>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx,
+                             Wq, ldw, M, Y, ldy, yvec);
+    return launch_kernel(k_gemm_bf16<false>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx, Wq,
+                         ldw, M, Y, ldy, yvec);
+}
+
+}  // namespace ttq

@@ -1,10 +1,26 @@
 // Kernel launchers (host side) used by the C ABI in ttq_api.cpp.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ttq {
+
+// Stage timing: the first kernel of a stage records `start` as it starts and
+// the last records `stop` as it ends (hipExtLaunchKernel stamps the dispatch
+// itself, so nothing extra is enqueued).  Null events: a plain launch.
+struct StageTimer {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t st, hipEvent_t e0,
+                                hipEvent_t e1, Args... args) {
+    hipExtLaunchKernelGGL(kern, grid, block, (std::uint32_t)lds, st, e0, e1, 0u, args...);
+    return hipGetLastError();
+}
 
 // Token-chunk split of the statistics reduction: returns the number of
 // chunks (fp64 partial rows) and the rows per chunk.
@@ -12,20 +28,49 @@ int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk);
 // K-slice split of the low-rank Z = A X pass.
 int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len);
 
+// At most this many fp64 partial rows of K channels in the stats workspace.
+constexpr int kMaxStatsChunks = 32;
+// Optional shrinkage output of the statistics pass: lambda = lambda_rel *
+// mean(ssq / T), finished by the last reduction workgroup.  bsum: ceil(K/64)
+// doubles; done: one counter (zeroed by the pass itself); lam: one double.
+struct StatsLam {
+    float lambda_rel;
+    double* bsum;
+    unsigned* done;
+    double* lam;
+};
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st);
+                        int accumulate, double* part, hipStream_t st, const StatsLam* lam = nullptr,
+                        StageTimer tm = {});
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float* s, hipStream_t st);
+// Scales evaluated inside the quantizer from the statistics (instead of a
+// given s): s[j] = awq_scale(ssq[j], tn, *lam, e), also stored to s_out.
+struct QScaleSrc {
+    const double* ssq;
+    const double* lam;
+    double tn;
+    double e;
+    float* s_out;
+};
 hipError_t launch_quantize(const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw,
                            const float* s, int bits, int group, const float* B, const float* A,
                            int rank, uint32_t* codes, uint16_t* scale, uint16_t* zero,
-                           hipStream_t st);
+                           uint16_t* wq, hipStream_t st, const QScaleSrc* qs = nullptr,
+                           StageTimer tm = {});
 hipError_t launch_qgemm(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                         const float* s, const uint32_t* codes, const uint16_t* scale,
                         const uint16_t* zero, int64_t M, int bits, int group, void* Y, bool yf32,
-                        int64_t ldy, hipStream_t st);
+                        int64_t ldy, uint16_t* wq, hipStream_t st, StageTimer tm = {});
+// Prompt-sized projections use the dequantized weight w~ ([M][K] bf16) and
+// the matrix-core GEMM; smaller ones (and fp32 X) the fused kernel.
+constexpr int64_t kDequantGemmMinT = 192;
+bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw);
+hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
+                            int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
+                            StageTimer tm = {});
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
-                          int64_t ldy, float* Zp, hipStream_t st);
+                          int64_t ldy, float* Zp, hipStream_t st, StageTimer tm = {});
 
 }  // namespace ttq

@@ -119,25 +119,29 @@ int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len) {
 template <int RMAX>
 static hipError_t launch_lr(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                             const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
-                            int64_t ldy, float* Zp, hipStream_t st) {
+                            int64_t ldy, float* Zp, hipStream_t st, StageTimer tm) {
     int64_t len = 0;
     const int ns = lowrank_slices(T, K, &len);
     dim3 gz((unsigned)((T + 63) / 64), (unsigned)ns);
-    if (xf32) k_lowrank_z<true, RMAX><<<gz, 64, 0, st>>>(X, T, K, ldx, A, rank, len, Zp);
-    else k_lowrank_z<false, RMAX><<<gz, 64, 0, st>>>(X, T, K, ldx, A, rank, len, Zp);
+    hipError_t e = xf32 ? launch_kernel(k_lowrank_z<true, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X, T, K,
+                                        ldx, A, rank, len, Zp)
+                        : launch_kernel(k_lowrank_z<false, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X, T, K,
+                                        ldx, A, rank, len, Zp);
+    if (e != hipSuccess) return e;
     dim3 gy((unsigned)((M + 63) / 64), (unsigned)((T + 63) / 64));
-    if (yf32) k_lowrank_y<true, RMAX><<<gy, 256, 0, st>>>(Zp, ns, B, rank, T, M, Y, ldy);
-    else k_lowrank_y<false, RMAX><<<gy, 256, 0, st>>>(Zp, ns, B, rank, T, M, Y, ldy);
-    return hipGetLastError();
+    return yf32 ? launch_kernel(k_lowrank_y<true, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, Zp, ns, B, rank,
+                                T, M, Y, ldy)
+                : launch_kernel(k_lowrank_y<false, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, Zp, ns, B, rank,
+                                T, M, Y, ldy);
 }
 
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
-                          int64_t ldy, float* Zp, hipStream_t st) {
+                          int64_t ldy, float* Zp, hipStream_t st, StageTimer tm) {
     // The accumulators are sized by the smallest of 8/16/32 that holds rank.
-    if (rank <= 8) return launch_lr<8>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
-    if (rank <= 16) return launch_lr<16>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
-    if (rank <= kMaxRank) return launch_lr<32>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st);
+    if (rank <= 8) return launch_lr<8>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
+    if (rank <= 16) return launch_lr<16>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
+    if (rank <= kMaxRank) return launch_lr<32>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
     return hipErrorInvalidValue;
 }
 

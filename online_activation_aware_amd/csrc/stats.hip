@@ -6,28 +6,33 @@
 //
 // k_stats_partial: a coalesced column reduction.  Each lane owns 8
 // consecutive channels (one 16-byte bf16 load per token row, or two for
-// fp32); the four waves of a workgroup stride over the rows of one token
-// chunk; squares are accumulated in fp64; the four wave partials are combined
-// through LDS in a fixed order and each workgroup writes one fp64 partial row
-// per chunk.  k_stats_final sums the chunk partials in chunk order.  No
-// atomics anywhere, so the result is bitwise reproducible.
+// fp32); the 16 waves of a workgroup stride over the rows of one token chunk;
+// squares are accumulated in fp64; the wave partials are combined through LDS
+// in a fixed order and each workgroup writes one fp64 partial row per chunk.
+// k_stats_final sums the chunk partials in chunk order.  Every sum has a
+// fixed order, so results are bitwise reproducible (the one atomic counter
+// only elects the workgroup that finishes the shrinkage mean).
 #include "common.hpp"
 #include "launch.hpp"
+#include "scales.hpp"
 
 namespace ttq {
 
-constexpr int kStatsThreads = 256;
+constexpr int kStatsThreads = 1024;         // 16 waves: all of a chunk's rows in flight at once
+constexpr int kStatsWaves = kStatsThreads / kWave;
 constexpr int kStatsChans = kWave * 8;      // channels per workgroup strip
 
 template <bool XF32>
 __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, int rows_per_chunk,
-    double* __restrict__ part) {
+    double* __restrict__ part, unsigned* __restrict__ done) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int64_t c0 = (int64_t)blockIdx.x * kStatsChans + lane * 8;
     const int64_t t0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t t1 = min(T, t0 + rows_per_chunk);
+    // The completion counter of the following reduction starts at zero.
+    if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *done = 0u;
 
     double acc[8];
 #pragma unroll
@@ -36,8 +41,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     if (c0 < K) {
         if constexpr (XF32) {
             const float* base = (const float*)X + c0;
-#pragma unroll 8
-            for (int64_t t = t0 + wave; t < t1; t += 4) {
+#pragma unroll 4
+            for (int64_t t = t0 + wave; t < t1; t += kStatsWaves) {
                 const f32x4* p = (const f32x4*)(base + t * ldx);
                 f32x4 a = ld_nc(p), b = ld_nc(p + 1);
 #pragma unroll
@@ -51,7 +56,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
         } else {
             const uint16_t* base = (const uint16_t*)X + c0;
 #pragma unroll 8
-            for (int64_t t = t0 + wave; t < t1; t += 4) {
+            for (int64_t t = t0 + wave; t < t1; t += kStatsWaves) {
                 u32x4 w = ld_nc((const u32x4*)(base + t * ldx));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -64,116 +69,148 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
         }
     }
 
-    __shared__ double red[4][kStatsChans];
+    __shared__ double red[kStatsWaves][kStatsChans];
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = acc[i];
     __syncthreads();
-    // 512 channel sums, two per thread; waves summed in order 0,1,2,3.
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = threadIdx.x + h * kStatsThreads;
+    // 512 channel sums; the 16 wave partials are added in wave order.
+    if (threadIdx.x < kStatsChans) {
+        const int c = threadIdx.x;
         const int64_t ch = (int64_t)blockIdx.x * kStatsChans + c;
         if (ch < K) {
             double s = red[0][c];
-            s += red[1][c];
-            s += red[2][c];
-            s += red[3][c];
+#pragma unroll
+            for (int w = 1; w < kStatsWaves; ++w) s += red[w][c];
             part[(int64_t)blockIdx.y * K + ch] = s;
         }
     }
 }
 
-// Sum of the chunk partials: a workgroup covers 64 channels; its four waves
-// take every fourth chunk and the four sums are added in wave order.
-__global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ part, int nchunks,
-                                                     int64_t K, double* __restrict__ ssq,
-                                                     int accumulate) {
-    __shared__ double red[4][64];
-    const int c = threadIdx.x & 63, p = threadIdx.x >> 6;
-    const int64_t j = (int64_t)blockIdx.x * 64 + c;
-    double s = 0.0;
+constexpr int kMaxLamBlocks = 4096;          // K <= 2^18
+
+// Sum of the chunk partials, in chunk order: thread <-> channel, 256 channels
+// (four 64-channel blocks) per workgroup.  With LAM, each wave also forms its
+// block's sum of c = ssq / n (cblock_sum order), and the last workgroup to
+// finish adds the block sums in block order and stores
+// lambda = lambda_rel * mean(c) in *lam.
+template <bool LAM>
+__global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ part, int nchunks, int64_t K,
+                                                     double* __restrict__ ssq, int accumulate, double tn,
+                                                     double lambda_rel, double* __restrict__ bsum,
+                                                     unsigned* __restrict__ done, double* __restrict__ lam) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    double tot = 0.0;
     if (j < K) {
-#pragma unroll 4
-        for (int ch = p; ch < nchunks; ch += 4) s += part[(int64_t)ch * K + j];
+#pragma unroll 8
+        for (int ch = 0; ch < nchunks; ++ch) tot += part[(int64_t)ch * K + j];
+        if (accumulate) tot = ssq[j] + tot;
+        ssq[j] = tot;
     }
-    red[p][c] = s;
-    __syncthreads();
-    if (p == 0 && j < K) {
-        double tot = red[0][c];
-        tot += red[1][c];
-        tot += red[2][c];
-        tot += red[3][c];
-        ssq[j] = accumulate ? ssq[j] + tot : tot;
+    if constexpr (LAM) {
+        __shared__ bool last;
+        const double bs = wave_sum_fixed(j < K ? tot / tn : 0.0);
+        const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+        if (lane == 0 && 64 * b < K) bsum[b] = bs;
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
+        __syncthreads();
+        if (last) {
+            // Every block sum is written (the other workgroups fenced before
+            // counting); gather them with parallel device-scope loads, then
+            // add them in block order.
+            __threadfence();
+            __shared__ double bl[kMaxLamBlocks];
+            const int64_t nb = (K + 63) / 64;
+            for (int64_t i = threadIdx.x; i < nb; i += 256)
+                bl[i] = __hip_atomic_load(bsum + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                double sum = 0.0;
+                for (int64_t i = 0; i < nb; ++i) sum += bl[i];
+                *lam = lambda_rel * (sum / (double)K);
+            }
+        }
     }
 }
 
-// [TTQ §method b2-b4]: c = ssq / T; lambda = lambda_rel * mean(c);
-// s = (c + lambda)^(alpha/2) in fp64, rounded once to fp32; 1 where c+lambda == 0.
-// Every workgroup forms the same mean(c) (same fixed summation order), then
-// the scales of its own 256 channels.
-constexpr int kScaleThreads = 256;
+// Standalone scales from ssq: one workgroup of 1024 threads.  The 16 waves
+// form the 64-channel block sums (cblock_sum) into LDS, thread 0 adds them in
+// block order, then every thread evaluates the scales of its channels.
+constexpr int kScaleThreads = 1024;
+constexpr int kMaxScaleBlocks = 4096;        // K <= 2^18
 
 __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __restrict__ ssq,
                                                               int64_t n_tokens, int64_t K,
                                                               double alpha, double lambda_rel,
                                                               float* __restrict__ s) {
-    __shared__ double red[kScaleThreads];
-    const int tid = threadIdx.x;
+    __shared__ double bs[kMaxScaleBlocks];
+    __shared__ double lam_s;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
     const double tn = (double)n_tokens;
-    double part = 0.0;
-    for (int64_t j = tid; j < K; j += kScaleThreads) part += ssq[j] / tn;
-    red[tid] = part;
+    const int64_t nb = (K + 63) / 64;
+    for (int64_t b = wave; b < nb; b += kScaleThreads / kWave) {
+        const double v = cblock_sum(ssq, b, K, tn, lane);
+        if (lane == 0) bs[b] = v;
+    }
     __syncthreads();
-    for (int w = kScaleThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        double sum = 0.0;
+        for (int64_t i = 0; i < nb; ++i) sum += bs[i];
+        lam_s = lambda_rel * (sum / (double)K);
     }
-    const double lam = lambda_rel * (red[0] / (double)K);
-    const double e = alpha / 2.0;
-    const int64_t j = (int64_t)blockIdx.x * kScaleThreads + tid;
-    if (j < K) {
-        const double cl = ssq[j] / tn + lam;
-        s[j] = cl == 0.0 ? 1.0f : (float)pow(cl, e);
-    }
+    __syncthreads();
+    const double lam = lam_s, e = alpha / 2.0;
+    for (int64_t j = threadIdx.x; j < K; j += kScaleThreads) s[j] = awq_scale(ssq[j], tn, lam, e);
 }
 
 // ------------------------------------------------------------------ host
 
 int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk) {
-    // At most 32 token chunks (the fp64 partials stay <= 32 K doubles, a small
-    // fraction of the bytes read), at least ~1024 workgroups where T allows,
-    // and whole multiples of the 4 waves' row stride.
+    // At most kMaxStatsChunks token chunks (the fp64 partials stay small next
+    // to X), at least ~256 workgroups (one per compute unit) where T allows,
+    // and whole multiples of the 16 waves' row stride.
     const int64_t strips = (K + kStatsChans - 1) / kStatsChans;
-    int64_t want = (1024 + strips - 1) / strips;
-    if (want > 32) want = 32;
+    int64_t want = (256 + strips - 1) / strips;
+    if (want > kMaxStatsChunks) want = kMaxStatsChunks;
     if (want < 1) want = 1;
     int64_t rows = (T + want - 1) / want;
-    rows = (rows + 3) / 4 * 4;
-    if (rows <= 0) rows = 4;
+    rows = (rows + kStatsWaves - 1) / kStatsWaves * kStatsWaves;
+    if (rows <= 0) rows = kStatsWaves;
     *rows_per_chunk = (int)rows;
     return T > 0 ? (int)((T + rows - 1) / rows) : 0;
 }
 
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st) {
+                        int accumulate, double* part, hipStream_t st, const StatsLam* lam, StageTimer tm) {
     int rows = 0;
     const int nchunks = stats_chunks(T, K, &rows);
+    unsigned* done = lam ? lam->done : nullptr;
     if (nchunks > 0) {
         dim3 grid((unsigned)((K + kStatsChans - 1) / kStatsChans), (unsigned)nchunks);
-        if (xf32)
-            k_stats_partial<true><<<grid, kStatsThreads, 0, st>>>(X, T, K, ldx, rows, part);
-        else
-            k_stats_partial<false><<<grid, kStatsThreads, 0, st>>>(X, T, K, ldx, rows, part);
+        hipError_t e = xf32 ? launch_kernel(k_stats_partial<true>, grid, dim3(kStatsThreads), 0, st, tm.start,
+                                            nullptr, X, T, K, ldx, rows, part, done)
+                            : launch_kernel(k_stats_partial<false>, grid, dim3(kStatsThreads), 0, st, tm.start,
+                                            nullptr, X, T, K, ldx, rows, part, done);
+        if (e != hipSuccess) return e;
     }
-    k_stats_final<<<(unsigned)((K + 63) / 64), 256, 0, st>>>(part, nchunks, K, ssq, accumulate);
-    return hipGetLastError();
+    const dim3 g((unsigned)((K + 255) / 256));
+    hipEvent_t e0 = nchunks > 0 ? nullptr : tm.start;
+    if (lam != nullptr)
+        return launch_kernel(k_stats_final<true>, g, dim3(256), 0, st, e0, tm.stop, (const double*)part, nchunks,
+                             K, ssq, accumulate, (double)T, (double)lam->lambda_rel, lam->bsum, lam->done,
+                             lam->lam);
+    return launch_kernel(k_stats_final<false>, g, dim3(256), 0, st, e0, tm.stop, (const double*)part, nchunks, K,
+                         ssq, accumulate, 1.0, 0.0, (double*)nullptr, (unsigned*)nullptr, (double*)nullptr);
 }
 
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float* s, hipStream_t st) {
-    k_awq_scales<<<(unsigned)((K + kScaleThreads - 1) / kScaleThreads), kScaleThreads, 0, st>>>(
-        ssq, n_tokens, K, (double)alpha, (double)lambda_rel, s);
-    return hipGetLastError();
+    return launch_kernel(k_awq_scales, dim3(1), dim3(kScaleThreads), 0, st, nullptr, nullptr, ssq, n_tokens, K,
+                         (double)alpha, (double)lambda_rel, s);
 }
 
 }  // namespace ttq

@@ -35,6 +35,7 @@ ttq_status device_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxK = (int64_t)1 << 18;    // input channels (block sums of the mean fit in LDS)
 constexpr int kMaxRank = 32;
 constexpr size_t kAlign = 256;
 
@@ -76,7 +77,7 @@ ttq_status check_matrix(const char* name, const void* p, int t, int64_t rows, in
 
 ttq_status check_quant_shape(int64_t M, int64_t K, int bits, int group) {
     TTQ_REQUIRE(dim_ok(M), "M out of range");
-    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 32 == 0, "K must be a positive multiple of 32");
+    TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 32 == 0, "K must be a positive multiple of 32, at most 2^18");
     if (!bits_ok(bits)) return fail(TTQ_ERR_INVALID, "bits must be 2, 3, 4 or 5 (got %d)", bits);
     if (!group_ok(group)) return fail(TTQ_ERR_INVALID, "group must be 16, 32, 64 or 128 (got %d)", group);
     TTQ_REQUIRE(K % group == 0, "K must be a multiple of the group size");
@@ -111,12 +112,19 @@ ttq_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 // The statistics use at most kMaxStatsChunks token chunks whatever T is, so
 // one workspace fits every prompt length.
-constexpr int kMaxStatsChunks = 32;
 size_t ws_stats(int64_t T, int64_t K) {
     if (T <= 0) return 0;
-    return round_up((size_t)kMaxStatsChunks * (size_t)K * sizeof(double));
+    return round_up((size_t)ttq::kMaxStatsChunks * (size_t)K * sizeof(double));
 }
-size_t ws_qgemm(int64_t K) { (void)K; return 0; }
+// Prompt-sized projections stage the dequantized weight (M x K bf16) in the
+// workspace; the size is requested whenever T allows that path.
+size_t ws_qgemm(int64_t T, int64_t K, int64_t M) {
+    if (T < ttq::kDequantGemmMinT) return 0;
+    return round_up((size_t)M * (size_t)K * sizeof(uint16_t));
+}
+bool use_dequant_gemm(int64_t T, bool xf32, int64_t K, int64_t ldx) {
+    return !xf32 && T >= ttq::kDequantGemmMinT && ttq::gemm_bf16_supported(T, K, ldx, K);
+}
 size_t ws_lowrank(int64_t T, int64_t K, int rank) {
     if (rank <= 0 || T <= 0) return 0;
     int64_t len = 0;
@@ -125,7 +133,7 @@ size_t ws_lowrank(int64_t T, int64_t K, int rank) {
 }
 
 struct StateLayout {
-    size_t ssq, s, codes, scale, zero, scratch, total;
+    size_t ssq, s, codes, scale, zero, bsum, done, lam, scratch, total;
 };
 StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, int rank) {
     StateLayout L{};
@@ -135,9 +143,12 @@ StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, i
     L.codes = off;   off += round_up((size_t)M * (size_t)(K * bits / 32) * sizeof(int32_t));
     L.scale = off;   off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
     L.zero = off;    off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
+    L.bsum = off;    off += round_up((size_t)((K + 63) / 64) * sizeof(double));
+    L.done = off;    off += kAlign;
+    L.lam = off;     off += kAlign;
     L.scratch = off;
     size_t scratch = ws_stats(T, K);
-    if (ws_qgemm(K) > scratch) scratch = ws_qgemm(K);
+    if (ws_qgemm(T, K, M) > scratch) scratch = ws_qgemm(T, K, M);
     if (ws_lowrank(T, K, rank) > scratch) scratch = ws_lowrank(T, K, rank);
     L.total = off + scratch;
     return L;
@@ -162,7 +173,7 @@ const char* ttq_status_str(int status) {
 const char* ttq_last_error(void) { return g_last_error.c_str(); }
 
 size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group, int rank) {
-    if (!dim_ok(T) || !dim_ok(M) || K <= 0 || K > kMaxDim || K % 32 || !bits_ok(bits) ||
+    if (!dim_ok(T) || !dim_ok(M) || K <= 0 || K > kMaxK || K % 32 || !bits_ok(bits) ||
         !group_ok(group) || K % group || rank < 0 || rank > kMaxRank)
         return 0;
     return state_layout(T, K, M, bits, group, rank).total;
@@ -172,7 +183,7 @@ ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, d
                      int accumulate, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     TTQ_REQUIRE(dim_ok(T), "T out of range");
-    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 8 == 0, "K must be a positive multiple of 8");
+    TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 8 == 0, "K must be a positive multiple of 8, at most 2^18");
     if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
     TTQ_REQUIRE(ssq != nullptr && aligned(ssq, 8), "ssq: null or not 8-byte aligned");
     const size_t need = T > 0 ? ws_stats(T, K) : 0;
@@ -186,7 +197,7 @@ ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, d
 ttq_status ttq_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                           float lambda_rel, float p, float* s, void* stream) {
     g_last_error.clear();
-    TTQ_REQUIRE(K > 0 && K <= kMaxDim, "K out of range");
+    TTQ_REQUIRE(K > 0 && K <= kMaxK, "K must be in [1, 2^18]");
     TTQ_REQUIRE(n_tokens > 0, "n_tokens must be positive");
     TTQ_REQUIRE(ssq != nullptr && aligned(ssq, 8), "ssq: null or not 8-byte aligned");
     TTQ_REQUIRE(s != nullptr && aligned(s, 16), "s: null or not 16-byte aligned");
@@ -209,7 +220,8 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
     if (M == 0) return TTQ_OK;
     if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, false)) return e;
     return device_status(ttq::launch_quantize(W, wt == TTQ_F32, M, K, ldw, s, bits, group, B, A, rank,
-                                              (uint32_t*)codes, scale_f16, zero_f16, as_stream(stream)),
+                                              (uint32_t*)codes, scale_f16, zero_f16, nullptr,
+                                              as_stream(stream)),
                          "ttq_quantize_groups launch");
 }
 
@@ -224,10 +236,12 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, c
     if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
     if (T == 0 || M == 0) return TTQ_OK;
     if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
-    if (ttq_status e = check_ws(ws, ws_bytes, ws_qgemm(K))) return e;
+    const bool dq = use_dequant_gemm(T, xt == TTQ_F32, K, ldx);
+    if (ttq_status e = check_ws(ws, ws_bytes, dq ? ws_qgemm(T, K, M) : 0)) return e;
     hipStream_t st = as_stream(stream);
     return device_status(ttq::launch_qgemm(X, xt == TTQ_F32, T, K, ldx, s, (const uint32_t*)codes,
-                                           scale_f16, zero_f16, M, bits, group, Y, yt == TTQ_F32, ldy, st),
+                                           scale_f16, zero_f16, M, bits, group, Y, yt == TTQ_F32, ldy,
+                                           dq ? (uint16_t*)ws : nullptr, st),
                          "ttq_qgemm launch");
 }
 
@@ -236,7 +250,7 @@ ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t 
                            size_t ws_bytes, void* stream) {
     g_last_error.clear();
     TTQ_REQUIRE(dim_ok(T) && dim_ok(M), "T or M out of range");
-    TTQ_REQUIRE(K > 0 && K <= kMaxDim && K % 8 == 0, "K must be a positive multiple of 8");
+    TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 8 == 0, "K must be a positive multiple of 8, at most 2^18");
     if (ttq_status e = check_lowrank(B, A, rank, false)) return e;
     if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
     if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
@@ -265,6 +279,9 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     TTQ_REQUIRE(a->codes == nullptr || aligned(a->codes, 16), "codes: not 16-byte aligned");
     TTQ_REQUIRE(a->scale_f16 == nullptr || aligned(a->scale_f16, 2), "scale_f16: misaligned");
     TTQ_REQUIRE(a->zero_f16 == nullptr || aligned(a->zero_f16, 2), "zero_f16: misaligned");
+    if (a->stage_events != nullptr)
+        for (int i = 0; i < TTQ_LINEAR_STAGE_EVENTS; ++i)
+            TTQ_REQUIRE(a->stage_events[i] != nullptr, "stage_events[%d]: null handle", i);
     if (a->T == 0) return TTQ_OK;   // no prompt tokens: nothing to estimate or project
 
     const StateLayout L = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank);
@@ -279,31 +296,66 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     hipStream_t st = as_stream(stream);
     const bool xf32 = a->xt == TTQ_F32;
 
+    // Stage i is timed by events (2i, 2i+1), stamped by the stage's first and
+    // last kernel; a stage that launches nothing records both as markers.
+    void* const* ev = a->stage_events;
+    auto timer = [&](int i) -> ttq::StageTimer {
+        if (ev == nullptr) return {};
+        return {(hipEvent_t)ev[2 * i], (hipEvent_t)ev[2 * i + 1]};
+    };
+    auto markers = [&](int i) -> ttq_status {
+        if (ev == nullptr) return TTQ_OK;
+        for (int k = 0; k < 2; ++k)
+            if (ttq_status e = device_status(hipEventRecord((hipEvent_t)ev[2 * i + k], st), "stage event"))
+                return e;
+        return TTQ_OK;
+    };
+    // Statistics; the reduction also finishes lambda = lambda_rel * mean(c).
+    ttq::StatsLam sl{a->lambda_rel, (double*)(w + L.bsum), (unsigned*)(w + L.done), (double*)(w + L.lam)};
     if (ttq_status e = device_status(
-            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st), "stats"))
+            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st, &sl, timer(0)),
+            "stats"))
         return e;
-    if (ttq_status e = device_status(
-            ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, s, st), "scales"))
-        return e;
-    if (a->M == 0) return TTQ_OK;
+    if (a->M == 0) {
+        // No rows to quantize: the scales still form part of the prompt state.
+        if (ttq_status e = device_status(ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, s, st),
+                                         "scales"))
+            return e;
+        for (int i = 1; i < 4; ++i)
+            if (ttq_status e = markers(i)) return e;
+        return TTQ_OK;
+    }
+    // The quantizer evaluates the scales of its channels from (ssq, lambda)
+    // with the same arithmetic as ttq_awq_scales, and stores s.
+    const ttq::QScaleSrc qs{ssq, sl.lam, (double)a->T, (double)a->alpha / 2.0, s};
+    // Prompt-sized projections: the quantizer also writes the dequantized
+    // weight (into the scratch area, free again once the statistics are
+    // reduced) and the projection is a plain matrix-core GEMM on it.
+    const bool dq = use_dequant_gemm(a->T, xf32, a->K, a->ldx);
+    uint16_t* wq = dq ? (uint16_t*)scratch : nullptr;
     if (ttq_status e = device_status(
             ttq::launch_quantize(a->W, a->wt == TTQ_F32, a->M, a->K, a->ldw, s, a->bits, a->group, a->B,
-                                 a->A, a->rank, (uint32_t*)codes, scale, zero, st),
+                                 a->A, a->rank, (uint32_t*)codes, scale, zero, wq, st, &qs, timer(1)),
             "quantize"))
         return e;
-    if (ttq_status e = device_status(
-            ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero,
-                              a->M, a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, st),
-            "qgemm"))
-        return e;
-    if (a->rank > 0) {
-        if (ttq_status e = device_status(
-                ttq::launch_lowrank(a->X, xf32, a->T, a->K, a->ldx, a->A, a->B, a->M, a->rank, a->Y,
-                                    a->yt == TTQ_F32, a->ldy, (float*)scratch, st),
-                "lowrank"))
+    if (dq) {
+        if (ttq_status e = device_status(ttq::launch_gemm_bf16((const uint16_t*)a->X, a->T, a->K, a->ldx, wq,
+                                                               a->K, a->M, a->Y, a->yt == TTQ_F32, a->ldy, st,
+                                                               timer(2)),
+                                         "gemm"))
             return e;
+    } else if (ttq_status e = device_status(
+                   ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero,
+                                     a->M, a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, nullptr, st,
+                                     timer(2)),
+                   "qgemm")) {
+        return e;
     }
-    return TTQ_OK;
+    if (a->rank > 0)
+        return device_status(ttq::launch_lowrank(a->X, xf32, a->T, a->K, a->ldx, a->A, a->B, a->M, a->rank, a->Y,
+                                                 a->yt == TTQ_F32, a->ldy, (float*)scratch, st, timer(3)),
+                             "lowrank");
+    return markers(3);
 }
 
 }  // extern "C"

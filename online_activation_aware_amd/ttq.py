@@ -41,6 +41,7 @@ class LinearArgs(ctypes.Structure):
         ("Y", ctypes.c_void_p), ("yt", ctypes.c_int), ("ldy", ctypes.c_int64),
         ("ssq", ctypes.c_void_p), ("s", ctypes.c_void_p), ("codes", ctypes.c_void_p),
         ("scale_f16", ctypes.c_void_p), ("zero_f16", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
     ]
 
 
@@ -206,10 +207,11 @@ def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: f
                lambda_rel: float, p: float = 2.0, B: Optional[torch.Tensor] = None,
                A: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
                y_dtype=torch.float32, ws: Optional[torch.Tensor] = None, state: Optional[dict] = None,
-               stream=None) -> torch.Tensor:
+               stream=None, stage_events=None) -> torch.Tensor:
     """One call for the whole layer.  ``state`` may hold preallocated output
     tensors ``ssq``, ``s``, ``codes``, ``scale_f16``, ``zero_f16`` that receive
-    the prompt's quantization state (for later decode-step ttq_qgemm calls)."""
+    the prompt's quantization state (for later decode-step ttq_qgemm calls).
+    ``stage_events``: optional StageEvents, recorded at the stage boundaries."""
     T, K = X.shape
     M = W.shape[0]
     rank = 0 if B is None else B.shape[1]
@@ -226,10 +228,66 @@ def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: f
         Y=_dev(Y, "Y"), yt=_dtype_code(Y), ldy=_ld(Y, "Y"),
         ssq=_dev(st.get("ssq"), "ssq"), s=_dev(st.get("s"), "s"), codes=_dev(st.get("codes"), "codes"),
         scale_f16=_dev(st.get("scale_f16"), "scale_f16"), zero_f16=_dev(st.get("zero_f16"), "zero_f16"),
+        stage_events=None if stage_events is None else ctypes.cast(stage_events.handles, ctypes.c_void_p),
     )
     wp, wn = _ws(ws, X.device)
     _check(lib().ttq_linear(ctypes.byref(a), wp, wn, _stream(stream)))
     return Y
+
+
+TTQ_LINEAR_STAGE_EVENTS = 8
+LINEAR_STAGES = ("stats", "quantize", "projection", "lowrank")
+
+_hip_handle = None
+
+
+def _hip() -> ctypes.CDLL:
+    """The HIP runtime already loaded by torch (same soname, one runtime)."""
+    global _hip_handle
+    if _hip_handle is None:
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipEventCreate.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip_handle = h
+    return _hip_handle
+
+
+class StageEvents:
+    """TTQ_LINEAR_STAGE_EVENTS timing events for ttq_linear(stage_events=...):
+    a (start, stop) pair per stage, stamped by the stage's own kernels."""
+
+    def __init__(self):
+        h = _hip()
+        self.handles = (ctypes.c_void_p * TTQ_LINEAR_STAGE_EVENTS)()
+        for i in range(TTQ_LINEAR_STAGE_EVENTS):
+            ev = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = ev
+
+    def stage_ms(self) -> dict:
+        """Milliseconds per stage (waits for the last event)."""
+        h = _hip()
+        if h.hipEventSynchronize(self.handles[-1]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = {}
+        for i, name in enumerate(LINEAR_STAGES):
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), self.handles[2 * i], self.handles[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = ms.value
+        return out
+
+    def __del__(self):
+        try:
+            h = _hip()
+            for ev in self.handles:
+                if ev:
+                    h.hipEventDestroy(ev)
+        except Exception:
+            pass
 
 
 def linear_state(T: int, K: int, M: int, bits: int, group: int, device="cuda") -> dict:

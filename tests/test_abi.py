@@ -52,6 +52,9 @@ def test_workspace_bytes(L):
     # at least the quantization state: ssq + s + codes + steps + zeros
     state = 4096 * 8 + 4096 * 4 + 4096 * 4096 * 4 // 8 + 2 * 4096 * 128 * 2
     assert n >= state and n % 256 == 0
+    # prompt-sized projections stage the dequantized weight (M x K bf16)
+    assert n >= state + 4096 * 4096 * 2
+    assert ttq.ttq_workspace_bytes(16, 4096, 4096, 4, 32, 0) < state + 4096 * 4096 * 2
     assert ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 16) >= ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 0)
     for bad in [(10, 100, 10, 4, 32, 0),     # K not a multiple of 32
                 (10, 128, 10, 6, 32, 0),     # bits
@@ -147,5 +150,10 @@ def test_lowrank_and_linear_reject(L):
     assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1
     a.bits = 4
     assert L.ttq_linear(ctypes.byref(a), FAKE, 16, None) == 1         # workspace too small
+    handles = (ctypes.c_void_p * ttq.TTQ_LINEAR_STAGE_EVENTS)(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE)
+    a.stage_events = ctypes.cast(handles, ctypes.c_void_p)
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1    # a null event handle
+    assert "stage_events" in _err(L)
+    a.stage_events = None
     a.T = 0
     assert L.ttq_linear(ctypes.byref(a), None, 0, None) == 0          # empty prompt

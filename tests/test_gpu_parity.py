@@ -192,7 +192,7 @@ def test_qgemm_parity(T, bits, group, K, xdt):
     assert err < (Y_TOL if xdt == "bf16" else 1e-4), err
 
 
-@pytest.mark.parametrize("Tn,M", [(1, 128), (5, 302), (129, 130), (16, 64)])
+@pytest.mark.parametrize("Tn,M", [(1, 128), (5, 302), (129, 130), (16, 64), (192, 130), (257, 302), (700, 77)])
 def test_qgemm_ragged_and_bf16_output(T, Tn, M):
     say(f"qgemm ragged T={Tn} M={M}")
     for ydt, tol in (("f32", Y_TOL), ("bf16", Y_TOL_BF16_OUT)):
@@ -244,6 +244,11 @@ E2E = [
     ("c3", dict(T=96, K=1024, M=320)),
     ("c4", dict(T=100, K=2048, M=256)),
     ("c5", dict(T=128, K=512, M=512)),
+    # prompt-sized T: the quantizer writes the dequantized weight, matrix-core GEMM
+    ("c2-long", dict(T=300, K=1024, M=288)),
+    ("c3-long", dict(T=400, K=1024, M=320)),
+    ("c4-long", dict(T=256, K=2048, M=256)),
+    ("c5-long", dict(T=260, K=512, M=512)),
 ]
 
 
@@ -259,7 +264,7 @@ def _run_linear(T, wl, d, B=None, A=None):
 @pytest.mark.parametrize("key,sizes", E2E, ids=[k for k, _ in E2E])
 def test_linear_end_to_end(T, key, sizes):
     say(f"linear e2e {key} {sizes}")
-    wl, d = _inputs(key, **sizes)
+    wl, d = _inputs(key.split("-")[0], **sizes)
     B = A = None
     if wl.rank:
         s0 = oracle.awq_scales(oracle.stats(d["X"], wl.xdtype), wl.T, wl.alpha, wl.lambda_rel)
@@ -292,6 +297,70 @@ def test_decode_steps_reuse_prompt_state(T):
         assert rel_fro(host(Yd), refd) < Y_TOL, td
 
 
+def test_linear_and_qgemm_share_the_dequantized_weight(T):
+    # For prompt-sized T the whole-layer call takes the dequantized weight
+    # from the quantizer, ttq_qgemm expands the stored codes itself; both
+    # must produce the same bf16 weight, hence bitwise the same Y.
+    say("linear vs qgemm on the prompt state")
+    wl, d = _inputs("c3", T=384, K=1024, M=320)
+    Y, st = _run_linear(T, wl, d)
+    ws = T.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    Yq = T.ttq_qgemm(to_dev(d["X"], "bf16"), st["s"], st["codes"], st["scale_f16"], st["zero_f16"],
+                     wl.M, wl.bits, wl.group, ws=ws)
+    assert torch.equal(Y, Yq)
+
+
+def test_linear_stage_events(T):
+    # Events recorded inside ttq_linear do not change the result and time
+    # every stage of the call.
+    say("linear stage events")
+    wl, d = _inputs("c2", T=512, K=1024, M=512)
+    Y0, _ = _run_linear(T, wl, d)
+    ev = T.StageEvents()
+    st = T.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    Y1 = T.ttq_linear(to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16"), wl.bits, wl.group, wl.alpha,
+                      wl.lambda_rel, state=st, stage_events=ev)
+    ms = ev.stage_ms()
+    assert set(ms) == set(T.LINEAR_STAGES)
+    assert all(v >= 0.0 for v in ms.values()) and ms["projection"] > 0.0
+    assert torch.equal(Y0, Y1)
+
+
+def test_linear_graph_replay(T):
+    # The whole-layer call captured in a graph (no memset nodes: the reduction
+    # counter is reset by the statistics kernel itself) and replayed several
+    # times with unrelated eager work in between; every replay must equal the
+    # eager result bitwise.
+    say("linear graph replay")
+    wl, d = _inputs("c2", T=300, K=1024, M=288)
+    X, W = to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16")
+    st = T.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    ws = T.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    Y = torch.empty((wl.T, wl.M), dtype=torch.float32, device="cuda")
+    T.ttq_linear(X, W, wl.bits, wl.group, wl.alpha, wl.lambda_rel, Y=Y, ws=ws, state=st)
+    torch.cuda.synchronize()
+    ref = Y.clone()
+    ref_state = {k: v.clone() for k, v in st.items()}
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cs):
+        T.ttq_linear(X, W, wl.bits, wl.group, wl.alpha, wl.lambda_rel, Y=Y, ws=ws, state=st)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Y.fill_(float("nan"))
+        for v in st.values():
+            v.zero_()
+        ws.fill_(0xA5)                      # stale scratch, including the counter
+        junk = torch.randn(1000, device="cuda") * 2
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref), rep
+        for k in st:
+            assert torch.equal(st[k], ref_state[k]), (rep, k)
+        assert torch.isfinite(junk).all()
+
+
 def test_run_twice_bitwise_identical(T):
     say("determinism")
     wl, d = _inputs("c3", T=96, K=1024, M=320)
@@ -302,14 +371,15 @@ def test_run_twice_bitwise_identical(T):
         assert torch.equal(st1[k], st2[k]), k
 
 
-def test_linear_strided_operands(T):
-    say("linear strided X/W/Y")
-    wl, d = _inputs("c2", T=70, K=512, M=200)
-    X = torch.zeros((70, 512 + 64), dtype=torch.bfloat16, device="cuda")
+@pytest.mark.parametrize("Tn", [70, 300])
+def test_linear_strided_operands(T, Tn):
+    say(f"linear strided X/W/Y T={Tn}")
+    wl, d = _inputs("c2", T=Tn, K=512, M=200)
+    X = torch.zeros((Tn, 512 + 64), dtype=torch.bfloat16, device="cuda")
     X[:, :512] = to_dev(d["X"], "bf16")
     W = torch.zeros((200, 512 + 32), dtype=torch.bfloat16, device="cuda")
     W[:, :512] = to_dev(d["W"], "bf16")
-    Yb = torch.full((70, 200 + 28), 5.0, dtype=torch.float32, device="cuda")
+    Yb = torch.full((Tn, 200 + 28), 5.0, dtype=torch.float32, device="cuda")
     T.ttq_linear(X[:, :512], W[:, :512], wl.bits, wl.group, wl.alpha, wl.lambda_rel, Y=Yb[:, :200])
     ref = oracle.linear(d["X"], "bf16", d["W"], "bf16", wl.bits, wl.group, wl.alpha, wl.lambda_rel)
     got = host(Yb)
