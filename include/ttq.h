@@ -131,7 +131,9 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  *   X: [T][K] (xt), s: [K], codes/scale/zero as produced by
  *   ttq_quantize_groups for (M, K, bits, group).  Y: [T][M] fp32 or bf16
  *   (yt), overwritten.  Y must not overlap any input.
- *   Two execution paths give the same bf16 weights: for bf16 X with
+ *   Three execution paths give the same bf16 weights: for T <= 128 with K a
+ *   multiple of 128 (at most 16384) the codes stream straight into registers
+ *   and are expanded there (decode steps, short prompts); for bf16 X with
  *   T >= 192 and K a multiple of 64 the weight is dequantized once into ws
  *   (M*K bf16) and multiplied by a matrix-core GEMM; otherwise codes are
  *   dequantized tile by tile inside the GEMM kernel.

@@ -69,6 +69,13 @@ bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw);
 hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
                             StageTimer tm = {});
+// Few-token projection (decode steps and short prompts): T <= kQgemvMaxT,
+// K a multiple of 128 and at most 16384.
+constexpr int64_t kQgemvMaxT = 128;
+bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32);
+hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
+                        const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
+                        int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm = {});
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                           int64_t ldy, float* Zp, hipStream_t st, StageTimer tm = {});

@@ -236,10 +236,15 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, c
     if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
     if (T == 0 || M == 0) return TTQ_OK;
     if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
-    const bool dq = use_dequant_gemm(T, xt == TTQ_F32, K, ldx);
+    const bool xf32 = xt == TTQ_F32;
+    const bool dq = use_dequant_gemm(T, xf32, K, ldx);
     if (ttq_status e = check_ws(ws, ws_bytes, dq ? ws_qgemm(T, K, M) : 0)) return e;
     hipStream_t st = as_stream(stream);
-    return device_status(ttq::launch_qgemm(X, xt == TTQ_F32, T, K, ldx, s, (const uint32_t*)codes,
+    if (ttq::qgemv_supported(T, K, ldx, xf32))
+        return device_status(ttq::launch_qgemv(X, xf32, T, K, ldx, s, (const uint32_t*)codes, scale_f16, zero_f16,
+                                               M, bits, group, Y, yt == TTQ_F32, ldy, st),
+                             "ttq_qgemm launch");
+    return device_status(ttq::launch_qgemm(X, xf32, T, K, ldx, s, (const uint32_t*)codes,
                                            scale_f16, zero_f16, M, bits, group, Y, yt == TTQ_F32, ldy,
                                            dq ? (uint16_t*)ws : nullptr, st),
                          "ttq_qgemm launch");
@@ -338,7 +343,13 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                                  a->A, a->rank, (uint32_t*)codes, scale, zero, wq, st, &qs, timer(1)),
             "quantize"))
         return e;
-    if (dq) {
+    if (ttq::qgemv_supported(a->T, a->K, a->ldx, xf32)) {
+        if (ttq_status e = device_status(
+                ttq::launch_qgemv(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero, a->M,
+                                  a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, st, timer(2)),
+                "qgemv"))
+            return e;
+    } else if (dq) {
         if (ttq_status e = device_status(ttq::launch_gemm_bf16((const uint16_t*)a->X, a->T, a->K, a->ldx, wq,
                                                                a->K, a->M, a->Y, a->yt == TTQ_F32, a->ldy, st,
                                                                timer(2)),

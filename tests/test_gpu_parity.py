@@ -200,6 +200,19 @@ def test_qgemm_ragged_and_bf16_output(T, Tn, M):
         assert rel_fro(got, ref) < tol
 
 
+@pytest.mark.parametrize("Tn", [1, 3, 16, 17, 33, 64, 65, 128])
+@pytest.mark.parametrize("bits,group", [(4, 32), (3, 16), (2, 64), (5, 128)])
+def test_qgemv_parity(T, Tn, bits, group):
+    # The few-token kernel (T <= 128, K % 128 == 0): K = 1152 gives the 16
+    # waves of a workgroup unequal chunk counts, M = 200 a partial row tile.
+    say(f"qgemv T={Tn} bits={bits} group={group}")
+    for xdt in ("bf16", "f32"):
+        key = "c1" if xdt == "f32" else "c2"
+        got, ref = _qgemm_case(T, key, Tn, 1152, 200, bits, group, xdt, "f32", seed=Tn + bits)
+        err = rel_fro(got, ref)
+        assert err < (Y_TOL if xdt == "bf16" else 1e-4), (xdt, err)
+
+
 def test_qgemm_identity_input_layout(T):
     # X = I: Y[t][o] = bf16((q - z) * step / s_t), element by element.
     say("qgemm identity layout")
