@@ -38,7 +38,11 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 # WRITE_SIZE, scaled by the factor a plain copy of known size gives), keyed by
 # the SHA-256 of the kernel source they were taken on.  A source change
 # invalidates them (traffic is then reported as null).
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # 4096->4096, T=2048 layer: profiles/ttq_linear_4096x4096_t2048_b4g32_pmc_traffic.txt
+    "e396b6d1af2807db": {"workload": "c2", "fetch_bytes": 167930678, "write_bytes": 35468590,
+                         "fetch_factor": 1.9999, "write_factor": 1.0},
+}
 
 
 def log(msg: str) -> None:
@@ -229,12 +233,17 @@ def main(argv=None) -> int:
     proj_us = stage_ms["projection"] * 1e3
     achieved = flops / (proj_us * 1e-6) / 1e12
     h = kernel_source_hash()
-    traffic = MEASURED_TRAFFIC.get(h)
+    tr = MEASURED_TRAFFIC.get(h)
+    traffic = tr["fetch_bytes"] + tr["write_bytes"] if tr and tr["workload"] == wl.key else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "k_gemm_bf16 (Y = X W~^T on the dequantized weight; bf16 MFMA 16x16x32, "
                           "fp32 accumulate, 128x256 tiles, buffer->LDS DMA)",
                 "flops_per_launch": flops, "avg_launch_us": round(proj_us, 2),
+                "traffic_detail": (None if traffic is None else
+                                   {"fetch_bytes": tr["fetch_bytes"], "write_bytes": tr["write_bytes"],
+                                    "operand_bytes": alg["projection"],
+                                    "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (1 GiB copy calibration)"}),
                 "timing": "kernel start/end stamped into HIP events by ttq_linear on its stream "
                           f"(hipExtLaunchKernel), averaged over {args.steps} instrumented steps"}
     breakdown = {}
