@@ -13,6 +13,7 @@
 // by buffer->LDS DMA into 3-slot rings issued two steps ahead (no staging
 // registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
 // one barrier per 64-deep K step, each wave waiting only for its own DMA.
+// Optionally the epilogue adds the low-rank term Z B^T (fp32) before the store.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_dma.hpp"
@@ -23,10 +24,11 @@ constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kBThreads = 512;
 constexpr int kBRowB = kBK * 2;                  // 128-byte LDS rows
 
-template <bool YF32>
+template <bool YF32, bool LR>
 __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const uint16_t* __restrict__ Wq,
-    int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec) {
+    int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec, const float* __restrict__ Z,
+    const float* __restrict__ Bm, int rank) {
     constexpr int NW = kBThreads / kWave;                       // 8 waves
     constexpr int XOPS = kBN * kBRowB / 1024 / NW;              // 1 KB DMA ops per wave for X (4)
     constexpr int WOPS = kBM * kBRowB / 1024 / NW;              // ... for W~ (2)
@@ -119,6 +121,38 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         if (kt + 2 < nk) step(kt + 4 < nk, sX2, sW2, sX1, sW1, kt + 2);
     }
 
+    if constexpr (LR) {
+        // [TTQ §method b5] low-rank term Y += B (A X) = Z B^T, in fp32, added
+        // before the store.  Every DMA has landed and every wave has passed
+        // the last barrier, so the ring slots are free: the tile's Z (256
+        // tokens) and B (128 rows), rank <= 32, are staged there transposed
+        // (rank-major), so lanes read consecutive tokens / rows.
+        float* zs = (float*)sX0;                  // [rank][256]
+        float* bs = (float*)sW0;                  // [rank][128]
+        for (int idx = tid; idx < rank * kBN; idx += kBThreads) {
+            const int k = idx / kBN, tt = idx % kBN;
+            zs[idx] = (t0 + tt < T) ? Z[(t0 + tt) * rank + k] : 0.0f;
+        }
+        for (int idx = tid; idx < rank * kBM; idx += kBThreads) {
+            const int k = idx / kBM, oo = idx % kBM;
+            bs[idx] = (o0 + oo < M) ? Bm[(o0 + oo) * rank + k] : 0.0f;
+        }
+        __syncthreads();
+        for (int k = 0; k < rank; ++k) {
+            float zt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zt[j] = zs[k * kBN + wn * 64 + 16 * j + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 bo = *(const f32x4*)(bs + k * kBM + wm * 64 + 16 * i + 4 * (lane >> 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(bo[r], zt[j], acc[i][j][r]);
+            }
+        }
+    }
+
     // Lane holds Y^T[o + r][t] for r = 0..3 (4 consecutive o of token t).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -139,14 +173,22 @@ bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw) {
 
 hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
-                            StageTimer tm) {
+                            StageTimer tm, const LowrankEpilogue* lr) {
     const int yvec = ((uintptr_t)Y % 16 == 0) && ((ldy * (yf32 ? 4 : 2)) % 16 == 0);
     dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((T + kBN - 1) / kBN));
-    if (yf32)
-        return launch_kernel(k_gemm_bf16<true>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx,
-                             Wq, ldw, M, Y, ldy, yvec);
-    return launch_kernel(k_gemm_bf16<false>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx, Wq,
-                         ldw, M, Y, ldy, yvec);
+    const float* Z = lr ? lr->Z : nullptr;
+    const float* B = lr ? lr->B : nullptr;
+    const int rank = lr ? lr->rank : 0;
+#define TTQ_B_LAUNCH(YF, LRF)                                                                              \
+    return launch_kernel(k_gemm_bf16<YF, LRF>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx, \
+                         Wq, ldw, M, Y, ldy, yvec, Z, B, rank)
+    if (rank > 0) {
+        if (yf32) TTQ_B_LAUNCH(true, true);
+        TTQ_B_LAUNCH(false, true);
+    }
+    if (yf32) TTQ_B_LAUNCH(true, false);
+    TTQ_B_LAUNCH(false, false);
+#undef TTQ_B_LAUNCH
 }
 
 }  // namespace ttq

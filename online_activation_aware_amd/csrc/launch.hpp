@@ -15,6 +15,13 @@ struct StageTimer {
     hipEvent_t stop = nullptr;
 };
 
+// Low-rank term added in the projection GEMM's epilogue: Y += Z B^T, fp32.
+struct LowrankEpilogue {
+    const float* Z;   // [T][rank]
+    const float* B;   // [M][rank]
+    int rank;
+};
+
 template <typename F, typename... Args>
 inline hipError_t launch_kernel(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1, Args... args) {
@@ -68,7 +75,7 @@ constexpr int64_t kDequantGemmMinT = 192;
 bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw);
 hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
-                            StageTimer tm = {});
+                            StageTimer tm = {}, const LowrankEpilogue* lr = nullptr);
 // Few-token projection (decode steps and short prompts): T <= kQgemvMaxT,
 // K a multiple of 128 and at most 16384.
 constexpr int64_t kQgemvMaxT = 128;
@@ -76,6 +83,11 @@ bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32);
 hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
                         const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
                         int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm = {});
+// Z = X A^T (fp32, [T][rank]) on the matrix cores, for bf16 X, K % 32 == 0
+// and a 16-byte-aligned A.
+bool lowrank_z_mfma_ok(bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A);
+hipError_t launch_lowrank_z(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A,
+                            int rank, float* Z, hipStream_t st, StageTimer tm = {});
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                           int64_t ldy, float* Zp, hipStream_t st, StageTimer tm = {});

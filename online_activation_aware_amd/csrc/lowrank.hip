@@ -3,18 +3,126 @@
 // [TTQ §method b5]: W = W_q + B A, so the quantized layer adds B (A X).
 // The term is kept in fp32 end to end: it can carry much of Y's energy.
 //
-// k_lowrank_z: one wave per 64 tokens and K slice (lane = token); A's values
-// are the same for every lane, so they come through scalar loads, and each
-// lane accumulates rank partial sums of its token over the slice.
+// k_lowrank_zm (bf16 X, K % 32 == 0): Z on the matrix cores.  A (fp32) is
+// split into three bf16 terms hi + mid + lo (the remainder is below 2^-24 of
+// A), X is bf16 already and the MFMA accumulates in fp32, so Z keeps fp32
+// accuracy.  A workgroup owns 16 tokens; its 16 waves take the 32-wide K steps
+// w, w + 16, ... and their tiles are added in wave order.
+// k_lowrank_z (fp32 X or other K): one wave per 64 tokens and K slice (lane =
+// token); A's values are the same for every lane, so they come through scalar
+// loads, and each lane accumulates rank partial sums of its token over the
+// slice.
 // k_lowrank_y: a 64 x 64 (tokens x rows) tile per workgroup; the slice
 // partials are summed in slice order into LDS together with the B rows, and
 // each thread adds a 4 x 4 block of B Z^T into Y.  No atomics.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace ttq {
 
 constexpr int kMaxRank = 32;
+
+constexpr int kZWaves = 16;
+
+template <int RT>
+__global__ __launch_bounds__(kZWaves * kWave) void k_lowrank_zm(const uint16_t* __restrict__ X, int64_t T,
+                                                                int64_t K, int64_t ldx,
+                                                                const float* __restrict__ A, int rank,
+                                                                float* __restrict__ Z) {
+    __shared__ f32x4 red[kZWaves][RT][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * 16;
+    const int64_t rows = min((int64_t)16, T - t0);
+    const rsrc_t rx = make_rsrc(X + t0 * ldx, ((rows - 1) * ldx + K) * 2);   // tokens >= T read as 0
+
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t nsteps = K / 32;
+    constexpr int U = 4;                          // steps whose loads are in flight together
+    for (int64_t sb = wave; sb < nsteps; sb += (int64_t)U * kZWaves) {
+        u32x4 xb[U];
+        f32x4 a0[U][RT], a1[U][RT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t step = sb + (int64_t)u * kZWaves;
+            const int64_t k0 = step * 32 + 8 * q;
+            const bool in = step < nsteps;
+            xb[u] = in ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rx, (int)((r16 * ldx + k0) * 2), 0, 0))
+                       : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int kr = 16 * rt + r16;         // rank row of this lane's operand
+                a0[u][rt] = a1[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (in && kr < rank) {
+                    a0[u][rt] = *(const f32x4*)(A + (int64_t)kr * K + k0);
+                    a1[u][rt] = *(const f32x4*)(A + (int64_t)kr * K + k0 + 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sb + (int64_t)u * kZWaves >= nsteps) break;   // wave-uniform
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float a[8] = {a0[u][rt][0], a0[u][rt][1], a0[u][rt][2], a0[u][rt][3],
+                                    a1[u][rt][0], a1[u][rt][1], a1[u][rt][2], a1[u][rt][3]};
+                u32x4 hi, mid, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pack_bf16x2(a[2 * e], a[2 * e + 1]);
+                    const float r0 = a[2 * e] - bf16lo_to_f32(hi[e]), r1 = a[2 * e + 1] - bf16hi_to_f32(hi[e]);
+                    mid[e] = pack_bf16x2(r0, r1);
+                    lo[e] = pack_bf16x2(r0 - bf16lo_to_f32(mid[e]), r1 - bf16hi_to_f32(mid[e]));
+                }
+                acc[rt] = mfma_16x16x32(hi, xb[u], acc[rt]);
+                acc[rt] = mfma_16x16x32(mid, xb[u], acc[rt]);
+                acc[rt] = mfma_16x16x32(lo, xb[u], acc[rt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) red[wave][rt][lane] = acc[rt];
+    __syncthreads();
+    // Lane of wave rt holds Z^T[16 rt + 4 q + i][t0 + r16], i = 0..3.
+    if (wave < RT) {
+        const int rt = wave;
+        f32x4 sum = red[0][rt][lane];
+        for (int w = 1; w < kZWaves; ++w) {
+            const f32x4 v = red[w][rt][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[i] += v[i];
+        }
+        const int64_t t = t0 + r16;
+        if (t < T) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 16 * rt + 4 * q + i;
+                if (k < rank) Z[t * rank + k] = sum[i];
+            }
+        }
+    }
+}
+
+bool lowrank_z_mfma_ok(bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A) {
+    return !xf32 && K % 32 == 0 && (int64_t)16 * ldx * 2 < ((int64_t)1 << 31) && T > 0 &&
+           (uintptr_t)A % 16 == 0;
+}
+
+hipError_t launch_lowrank_z(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A,
+                            int rank, float* Z, hipStream_t st, StageTimer tm) {
+    if (!lowrank_z_mfma_ok(xf32, T, K, ldx, A)) return hipErrorInvalidValue;
+    const dim3 g((unsigned)((T + 15) / 16));
+    if (rank <= 16)
+        return launch_kernel(k_lowrank_zm<1>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop,
+                             (const uint16_t*)X, T, K, ldx, A, rank, Z);
+    return launch_kernel(k_lowrank_zm<2>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop, (const uint16_t*)X,
+                         T, K, ldx, A, rank, Z);
+}
 
 template <bool XF32, int RMAX>
 __global__ __launch_bounds__(64) void k_lowrank_z(const void* __restrict__ X, int64_t T, int64_t K,
@@ -120,19 +228,24 @@ template <int RMAX>
 static hipError_t launch_lr(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                             const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                             int64_t ldy, float* Zp, hipStream_t st, StageTimer tm) {
-    int64_t len = 0;
-    const int ns = lowrank_slices(T, K, &len);
-    dim3 gz((unsigned)((T + 63) / 64), (unsigned)ns);
-    hipError_t e = xf32 ? launch_kernel(k_lowrank_z<true, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X, T, K,
-                                        ldx, A, rank, len, Zp)
-                        : launch_kernel(k_lowrank_z<false, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X, T, K,
-                                        ldx, A, rank, len, Zp);
-    if (e != hipSuccess) return e;
+    int ns = 1;
+    if (lowrank_z_mfma_ok(xf32, T, K, ldx, A)) {
+        if (hipError_t e = launch_lowrank_z(X, xf32, T, K, ldx, A, rank, Zp, st, {tm.start, nullptr})) return e;
+    } else {
+        int64_t len = 0;
+        ns = lowrank_slices(T, K, &len);
+        dim3 gz((unsigned)((T + 63) / 64), (unsigned)ns);
+        hipError_t e = xf32 ? launch_kernel(k_lowrank_z<true, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X,
+                                            T, K, ldx, A, rank, len, Zp)
+                            : launch_kernel(k_lowrank_z<false, RMAX>, gz, dim3(64), 0, st, tm.start, nullptr, X,
+                                            T, K, ldx, A, rank, len, Zp);
+        if (e != hipSuccess) return e;
+    }
     dim3 gy((unsigned)((M + 63) / 64), (unsigned)((T + 63) / 64));
-    return yf32 ? launch_kernel(k_lowrank_y<true, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, Zp, ns, B, rank,
-                                T, M, Y, ldy)
-                : launch_kernel(k_lowrank_y<false, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, Zp, ns, B, rank,
-                                T, M, Y, ldy);
+    return yf32 ? launch_kernel(k_lowrank_y<true, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, (const float*)Zp,
+                                ns, B, rank, T, M, Y, ldy)
+                : launch_kernel(k_lowrank_y<false, RMAX>, gy, dim3(256), 0, st, nullptr, tm.stop, (const float*)Zp,
+                                ns, B, rank, T, M, Y, ldy);
 }
 
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,

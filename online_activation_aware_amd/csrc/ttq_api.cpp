@@ -148,7 +148,10 @@ StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, i
     L.lam = off;     off += kAlign;
     L.scratch = off;
     size_t scratch = ws_stats(T, K);
-    if (ws_qgemm(T, K, M) > scratch) scratch = ws_qgemm(T, K, M);
+    // prompt-sized projections: the dequantized weight, then Z = X A^T for
+    // the low-rank epilogue
+    const size_t proj = ws_qgemm(T, K, M) + (rank > 0 && T > 0 ? round_up((size_t)T * rank * sizeof(float)) : 0);
+    if (proj > scratch) scratch = proj;
     if (ws_lowrank(T, K, rank) > scratch) scratch = ws_lowrank(T, K, rank);
     L.total = off + scratch;
     return L;
@@ -350,11 +353,24 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                 "qgemv"))
             return e;
     } else if (dq) {
+        // With low-rank factors: Z = X A^T on the matrix cores first, then the
+        // GEMM adds Z B^T in its epilogue (no second pass over Y).
+        ttq::LowrankEpilogue lre{nullptr, a->B, a->rank};
+        const bool fuse = a->rank > 0 && ttq::lowrank_z_mfma_ok(xf32, a->T, a->K, a->ldx, a->A);
+        if (fuse) {
+            float* Z = (float*)((char*)scratch + ws_qgemm(a->T, a->K, a->M));
+            if (ttq_status e = device_status(
+                    ttq::launch_lowrank_z(a->X, xf32, a->T, a->K, a->ldx, a->A, a->rank, Z, st, timer(3)),
+                    "lowrank Z"))
+                return e;
+            lre.Z = Z;
+        }
         if (ttq_status e = device_status(ttq::launch_gemm_bf16((const uint16_t*)a->X, a->T, a->K, a->ldx, wq,
                                                                a->K, a->M, a->Y, a->yt == TTQ_F32, a->ldy, st,
-                                                               timer(2)),
+                                                               timer(2), fuse ? &lre : nullptr),
                                          "gemm"))
             return e;
+        if (fuse) return TTQ_OK;
     } else if (ttq_status e = device_status(
                    ttq::launch_qgemm(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero,
                                      a->M, a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, nullptr, st,

@@ -232,9 +232,19 @@ def test_qgemm_identity_input_layout(T):
 
 # ---------------------------------------------------------------- lowrank
 
-@pytest.mark.parametrize("xdt,rank", [("bf16", 16), ("f32", 7), ("bf16", 32)])
-def test_lowrank_add_parity(T, xdt, rank):
-    say(f"lowrank_add xdt={xdt} rank={rank}")
+def _offset_dev(a: np.ndarray) -> torch.Tensor:
+    """fp32 device copy whose data starts 4 bytes past a 16-byte boundary."""
+    buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).ravel()).to("cuda")
+    return buf[1:].view(a.shape)
+
+
+@pytest.mark.parametrize("xdt,rank,a_off", [("bf16", 16, False), ("f32", 7, False), ("bf16", 32, False),
+                                            ("bf16", 16, True), ("bf16", 5, False)])
+def test_lowrank_add_parity(T, xdt, rank, a_off):
+    # bf16 X with an aligned A runs Z on the matrix cores; fp32 X or an A
+    # that is not 16-byte aligned runs the K-slice kernel.
+    say(f"lowrank_add xdt={xdt} rank={rank} A offset={a_off}")
     rng = np.random.default_rng(rank)
     Tn, K, M = 150, 512, 200
     X = synth.encode(rng.standard_normal((Tn, K)), xdt)
@@ -245,8 +255,10 @@ def test_lowrank_add_parity(T, xdt, rank):
     ref = Y0.astype(np.float64) + (x @ A.astype(np.float64).T) @ B.astype(np.float64).T
     Y = f32_dev(Y0)
     ws = T.workspace(Tn, K, M, 2, 32, rank)
-    T.ttq_lowrank_add(to_dev(X, xdt), f32_dev(A), f32_dev(B), Y, ws=ws)
-    assert rel_fro(host(Y), ref) < 1e-5
+    T.ttq_lowrank_add(to_dev(X, xdt), _offset_dev(A) if a_off else f32_dev(A), f32_dev(B), Y, ws=ws)
+    got = host(Y)
+    assert rel_fro(got, ref) < 1e-5
+    assert rel_fro(got.astype(np.float64) - Y0, ref - Y0) < 1e-5     # the low-rank term itself
 
 
 # ------------------------------------------------------------ end to end
@@ -295,6 +307,22 @@ def test_linear_end_to_end(T, key, sizes):
     err = rel_fro(host(Y), ref["Y"])
     say(f"  Y rel err {err:.3e}")
     assert err < Y_TOL
+
+
+def test_linear_lowrank_unaligned_factor(T):
+    # Prompt-sized T with an A that is not 16-byte aligned: the low-rank term
+    # is added by the standalone kernels after the GEMM instead of its epilogue.
+    say("linear low-rank, unaligned A")
+    wl, d = _inputs("c5", T=260, K=512, M=512)
+    s0 = oracle.awq_scales(oracle.stats(d["X"], wl.xdtype), wl.T, wl.alpha, wl.lambda_rel)
+    B, A = oracle.lowrank_factors(d["W"], wl.wdtype, s0, wl.rank)
+    ref = oracle.linear(d["X"], wl.xdtype, d["W"], wl.wdtype, wl.bits, wl.group, wl.alpha,
+                        wl.lambda_rel, B=B, A=A)
+    Y = T.ttq_linear(to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16"), wl.bits, wl.group, wl.alpha,
+                     wl.lambda_rel, B=f32_dev(B), A=_offset_dev(A))
+    assert rel_fro(host(Y), ref["Y"]) < Y_TOL
+    Y2, _ = _run_linear(T, wl, d, B, A)     # aligned: fused epilogue
+    assert rel_fro(host(Y2), host(Y)) < 1e-5
 
 
 def test_decode_steps_reuse_prompt_state(T):
