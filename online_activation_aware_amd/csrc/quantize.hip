@@ -7,9 +7,9 @@
 // Mapping: a workgroup (4 waves) owns a strip of 512 input channels and a
 // block of output rows; lane l owns 8 consecutive channels (one 16-byte bf16
 // load, two for fp32), so a group of g channels spans g/8 adjacent lanes and
-// its min/max needs log2(g/8) xor-shuffles.  Four adjacent lanes hold 32
-// codes = `bits` int32 words, assembled with quad shuffles and written by the
-// first `bits` lanes of the quad.  With low-rank factors, the strip of A
+// its min/max needs log2(g/8) DPP lane exchanges.  Four adjacent lanes hold
+// 32 codes = `bits` int32 words, assembled with quad broadcasts and written
+// by the first `bits` lanes of the quad.  With low-rank factors, the strip of A
 // (rank x 512 fp32) is staged once in LDS and reused for every row.
 //
 // Optionally the kernel also writes the dequantized weight of [TTQ §method b1]
@@ -17,6 +17,7 @@
 // (1/s)), dense [M][K] bf16: the operand of the prompt-sized projection, so
 // that the codes need not be read and expanded a second time.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -27,8 +28,46 @@ namespace ttq {
 constexpr int kQThreads = 256;
 constexpr int kQChans = kWave * 8;
 
+// Cross-lane moves through DPP (they run in the VALU pipeline, no LDS round
+// trip).  Quad permutations: lane i of each quad reads lane perm[i]
+// (control perm0 | perm1 << 2 | perm2 << 4 | perm3 << 6); row mirrors
+// reverse 8 or 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;     // [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane l of 8 <- lane 7 - l
+constexpr int kDppMirror = 0x140;      // lane l of 16 <- lane 15 - l
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, dpp_u<CTRL>(__builtin_bit_cast(uint32_t, x)));
+}
+
+// min/max over the GL = GROUP/8 lanes of a group (aligned runs of GL lanes).
+template <int GL>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+    static_assert(GL == 2 || GL == 4 || GL == 8 || GL == 16, "lanes per group");
+    mn = fminf(mn, dpp_f<kDppQuadXor1>(mn));
+    mx = fmaxf(mx, dpp_f<kDppQuadXor1>(mx));
+    if constexpr (GL >= 4) {
+        mn = fminf(mn, dpp_f<kDppQuadXor2>(mn));
+        mx = fmaxf(mx, dpp_f<kDppQuadXor2>(mx));
+    }
+    if constexpr (GL >= 8) {             // each quad holds its own range: pair it with the mirrored quad
+        mn = fminf(mn, dpp_f<kDppHalfMirror>(mn));
+        mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
+    }
+    if constexpr (GL >= 16) {
+        mn = fminf(mn, dpp_f<kDppMirror>(mn));
+        mx = fmaxf(mx, dpp_f<kDppMirror>(mx));
+    }
+}
+
 // Group RTN of one lane's 8 values and packing of the quad's 32 codes.
-// All 64 lanes of the wave must call this together (it shuffles).
+// All 64 lanes of the wave must call this together (cross-lane moves).
 template <int BITS, int GROUP>
 __device__ __forceinline__ void quantize_and_store(const float (&v)[8], bool active, int lane, int64_t cu,
                                                    int64_t col, int64_t o, int64_t words_per_row,
@@ -41,27 +80,27 @@ __device__ __forceinline__ void quantize_and_store(const float (&v)[8], bool act
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-#pragma unroll
-    for (int m = 1; m < GL; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-    }
+    group_minmax<GL>(mn, mx);
     mn = fminf(0.0f, mn);
     mx = fmaxf(0.0f, mx);
-    const float d32 = (mx - mn) / QMAX;
+    const float d32 = (mx - mn) / QMAX;           // correctly rounded
     const uint16_t dh = d32 == 0.0f ? (uint16_t)0x3C00 : f32_to_f16_up(d32);
     const float df = f16_to_f32(dh);
     const float z = fminf(fmaxf(rintf((-mn) / df), 0.0f), QMAX);
-    const float inv = 1.0f / df;
+    // Codes decided on v * (1/step) (v_rcp_f32, <= 1 ulp): only values within
+    // ~1e-7 of a step from a rounding boundary can differ from a division.
+    const float inv = __builtin_amdgcn_rcpf(df);
 
-    uint64_t field = 0;
+    // 8 codes of 8*BITS bits; a NaN value gives NaN + z, which the clamp's
+    // v_max_f32 turns into 0.
+    typedef typename std::conditional<(8 * BITS <= 32), uint32_t, uint64_t>::type field_t;
+    field_t field = 0;
     float qv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float q = fminf(fmaxf(rintf(v[i] * inv) + z, 0.0f), QMAX);
-        q = (v[i] != v[i]) ? 0.0f : q;
+        const float q = fminf(fmaxf(rintf(v[i] * inv) + z, 0.0f), QMAX);
         qv[i] = q;
-        field |= (uint64_t)(uint32_t)q << (BITS * i);
+        field |= (field_t)(uint32_t)q << (BITS * i);
     }
     if (wq != nullptr && active) {
         // (q - z) * step is exact in fp32 (a small integer times an fp16 value).
@@ -72,15 +111,22 @@ __device__ __forceinline__ void quantize_and_store(const float (&v)[8], bool act
         *(u32x4*)(wq + o * K + col) = pk;
     }
 
-    // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words.
-    const int qbase = lane & ~3;
+    // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words; every lane
+    // of the quad receives the quad's four fields by quad broadcasts.
     uint64_t fq[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint64_t lo = (uint32_t)__shfl((int)(uint32_t)field, qbase + k);
-        uint64_t hi = 0;
-        if constexpr (BITS * 8 > 32) hi = (uint32_t)__shfl((int)(uint32_t)(field >> 32), qbase + k);
-        fq[k] = lo | (hi << 32);
+    {
+        const uint32_t lo = (uint32_t)field;
+        fq[0] = dpp_u<0x00>(lo);
+        fq[1] = dpp_u<0x55>(lo);
+        fq[2] = dpp_u<0xAA>(lo);
+        fq[3] = dpp_u<0xFF>(lo);
+        if constexpr (8 * BITS > 32) {
+            const uint32_t hi = (uint32_t)((uint64_t)field >> 32);
+            fq[0] |= (uint64_t)dpp_u<0x00>(hi) << 32;
+            fq[1] |= (uint64_t)dpp_u<0x55>(hi) << 32;
+            fq[2] |= (uint64_t)dpp_u<0xAA>(hi) << 32;
+            fq[3] |= (uint64_t)dpp_u<0xFF>(hi) << 32;
+        }
     }
     auto word = [&](int j) -> uint32_t {
         uint32_t wv = 0;
@@ -152,7 +198,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     extern __shared__ float sA[];                 // [rank][kQChans] when LOWRANK
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // row addressing stays scalar
     const int64_t cu = (int64_t)blockIdx.x * kWave + lane;   // 8-channel unit in the row
     const int64_t col = cu * 8;
     const bool active = col < K;
@@ -199,59 +245,66 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const int64_t words_per_row = K * BITS / 32;
     const int64_t groups_per_row = K / GROUP;
 
-    // Rows per wave whose loads are in flight together.
+    // A row block is WSTRIDE x RB rows: each wave takes RB of them (a batch).
+    // The workgroup walks row blocks rb = blockIdx.y, + gridDim.y, ... (the
+    // grid is sized to the number of workgroups the device holds at once),
+    // and each wave issues the loads of its next batch before it processes
+    // the current one, so loads stay in flight while the VALU works.
     constexpr int RB = (LOWRANK || WF32) ? 4 : 8;
     constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
-    // Row blocks rb = blockIdx.y, + gridDim.y, ... (the grid is sized to the
-    // number of workgroups the device holds at once).
     const int64_t nrb = (M + rows_per_block - 1) / rows_per_block;
-    for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
-        const int64_t row0 = rb * rows_per_block;
-        const int64_t row1 = min(M, row0 + rows_per_block);
-        for (int64_t ob = row0 + wave; ob < row1; ob += WSTRIDE * RB) {
-            RawRow<WF32> raw[RB];
+    auto load_batch = [&](RawRow<WF32> (&dst)[RB], int64_t rb) __attribute__((always_inline)) {
+        const int64_t ob = rb * rows_per_block + wave;
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int64_t o = ob + (int64_t)WSTRIDE * r;
-                if (active && o < row1) {
-                    load_row<WF32>(raw[r], W, o, ldw, col);
-                } else {
-                    raw[r].a = u32x4{0u, 0u, 0u, 0u};
-                    raw[r].b = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int64_t o = ob + (int64_t)WSTRIDE * r;
-                if (o >= row1) break;                 // wave-uniform
-                float wv[8];
-                unpack_row<WF32>(raw[r], wv);
-                float v[8];
-                if constexpr (LOWRANK) {
-                    double acc[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = (double)wv[i];
-                    const float* Brow = B + o * rank;
-                    for (int k = 0; k < rank; ++k) {
-                        const double nb = -(double)Brow[k];
-                        const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
-                        f32x4 a0 = ak[0], a1 = ak[1];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            acc[i] = __builtin_fma(nb, (double)a0[i], acc[i]);
-                            acc[4 + i] = __builtin_fma(nb, (double)a1[i], acc[4 + i]);
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] = (float)(acc[i] * (double)sc[i]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] = wv[i] * sc[i];
-                }
-                quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
-                                                codes, scale, zero, sinv, wq, K);
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (rb < nrb && active && o < M) {
+                load_row<WF32>(dst[r], W, o, ldw, col);
+            } else {
+                dst[r].a = u32x4{0u, 0u, 0u, 0u};
+                dst[r].b = u32x4{0u, 0u, 0u, 0u};
             }
         }
+    };
+    RawRow<WF32> cur[RB];
+    load_batch(cur, blockIdx.y);
+    for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+        RawRow<WF32> nxt[RB];
+        load_batch(nxt, rb + gridDim.y);
+        const int64_t ob = rb * rows_per_block + wave;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (o >= M) break;                    // wave-uniform
+            float wv[8];
+            unpack_row<WF32>(cur[r], wv);
+            float v[8];
+            if constexpr (LOWRANK) {
+                double acc[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = (double)wv[i];
+                const float* Brow = B + o * rank;
+                for (int k = 0; k < rank; ++k) {
+                    const double nb = -(double)Brow[k];
+                    const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
+                    f32x4 a0 = ak[0], a1 = ak[1];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[i] = __builtin_fma(nb, (double)a0[i], acc[i]);
+                        acc[4 + i] = __builtin_fma(nb, (double)a1[i], acc[4 + i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[i] * (double)sc[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = wv[i] * sc[i];
+            }
+            quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
+                                            codes, scale, zero, sinv, wq, K);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) cur[r] = nxt[r];
     }
 }
 
@@ -261,9 +314,9 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
                             uint32_t* codes, uint16_t* scale, uint16_t* zero, uint16_t* wq,
                             const QScaleSrc* qs, hipStream_t st, StageTimer tm) {
     const bool lr = rank > 0;
-    // Rows per block: one batch of loads per wave (4 waves x 8 rows for
-    // bf16, x 4 for fp32); with low-rank factors more rows amortise staging A.
-    const int rows = lr ? 64 : (wf32 ? 16 : 32);
+    // Rows per block: one batch per wave (4 waves x 8 rows for bf16, x 4 for
+    // fp32 or with low-rank factors).
+    const int rows = (lr || wf32) ? 16 : 32;
     const int64_t strips = (K + kQChans - 1) / kQChans;
     const int64_t nrb = (M + rows - 1) / rows;
     const size_t lds = lr ? (size_t)rank * kQChans * sizeof(float) : 0;
@@ -300,6 +353,7 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
     } else {
         if (lr) { TTQ_Q_LAUNCH2(false, true); } else { TTQ_Q_LAUNCH2(false, false); }
     }
+
 #undef TTQ_Q_LAUNCH2
 #undef TTQ_Q_LAUNCH
     return hipGetLastError();

@@ -11,7 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/ttq.h"
+#include "ttq.h"
 #include "launch.hpp"
 
 namespace {
