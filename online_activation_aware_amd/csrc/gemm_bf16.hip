@@ -8,8 +8,9 @@
 // that of the fused dequantize-in-LDS kernel, so both paths see identical
 // bf16 weights.
 //
-// Tiling: 128 output rows x 256 tokens per workgroup, 8 waves (2 per SIMD),
-// each 64 x 64 (4 x 4 MFMA 16x16x32 per 32-deep slice).  Both operands arrive
+// Tiling: 128 output rows x 256 tokens per workgroup (128 x 128 when the grid
+// would otherwise leave most compute units idle), 8 waves (2 per SIMD), each
+// 64 x 64 (or 64 x 32): 4 x 4 (4 x 2) MFMA 16x16x32 per 32-deep slice.  Both operands arrive
 // by buffer->LDS DMA into 3-slot rings issued two steps ahead (no staging
 // registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
 // one barrier per 64-deep K step, each wave waiting only for its own DMA.
@@ -20,22 +21,24 @@
 
 namespace ttq {
 
-constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kBM = 128, kBK = 64;            // token tile BN: 256, or 128 for small grids
 constexpr int kBThreads = 512;
 constexpr int kBRowB = kBK * 2;                  // 128-byte LDS rows
 
-template <bool YF32, bool LR>
+template <int BN, bool YF32, bool LR>
 __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const uint16_t* __restrict__ Wq,
     int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec, const float* __restrict__ Z,
     const float* __restrict__ Bm, int rank) {
     constexpr int NW = kBThreads / kWave;                       // 8 waves
-    constexpr int XOPS = kBN * kBRowB / 1024 / NW;              // 1 KB DMA ops per wave for X (4)
+    constexpr int WT = BN / 4;                                  // tokens per wave (64 or 32)
+    constexpr int FB = WT / 16;                                 // token fragments per wave
+    constexpr int XOPS = BN * kBRowB / 1024 / NW;               // 1 KB DMA ops per wave for X (4 or 2)
     constexpr int WOPS = kBM * kBRowB / 1024 / NW;              // ... for W~ (2)
     constexpr int OPS = XOPS + WOPS;
-    __shared__ __attribute__((aligned(1024))) uint8_t sX0[kBN * kBRowB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sX1[kBN * kBRowB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sX2[kBN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX0[BN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX1[BN * kBRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX2[BN * kBRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sW0[kBM * kBRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sW1[kBM * kBRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sW2[kBM * kBRowB];
@@ -43,10 +46,10 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 2, wn = wave & 3;      // 2 x 4 waves of 64 x 64
+    const int wm = wave >> 2, wn = wave & 3;      // 2 x 4 waves of 64 x WT
     const int64_t o0 = (int64_t)blockIdx.x * kBM;
-    const int64_t t0 = (int64_t)blockIdx.y * kBN;
-    const int rows_x = (int)min((int64_t)kBN, T - t0);
+    const int64_t t0 = (int64_t)blockIdx.y * BN;
+    const int rows_x = (int)min((int64_t)BN, T - t0);
     const int rows_w = (int)min((int64_t)kBM, M - o0);
     const rsrc_t rx = make_rsrc(X + t0 * ldx, ((int64_t)(rows_x - 1) * ldx + K) * 2);
     const rsrc_t rw = make_rsrc(Wq + o0 * ldw, ((int64_t)(rows_w - 1) * ldw + K) * 2);
@@ -59,11 +62,11 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const int woff0 = ((wave * 8 * WOPS + rl) * (int)ldw + 8 * ch) * 2;
     const int xrow8 = 8 * (int)ldx * 2, wrow8 = 8 * (int)ldw * 2;
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][FB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto issue = [&](uint8_t* xd, uint8_t* wd, int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
@@ -74,21 +77,21 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
             dma_to_lds<16>(rw, wd + (wave * WOPS + i) * 1024, woff0 + i * wrow8, (int)k0 * 2);
     };
     auto compute = [&](const uint8_t* xs, const uint8_t* ws) __attribute__((always_inline)) {
-        u32x4 a[2][4], b[2][4];
+        u32x4 a[2][4], b[2][FB];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int c = 4 * kk + (lane >> 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[kk][i] = *(const u32x4*)(ws + lds_swz(wm * 64 + 16 * i + (lane & 15), c));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[kk][j] = *(const u32x4*)(xs + lds_swz(wn * 64 + 16 * j + (lane & 15), c));
+            for (int j = 0; j < FB; ++j) b[kk][j] = *(const u32x4*)(xs + lds_swz(wn * WT + 16 * j + (lane & 15), c));
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a[kk][i], b[kk][j], acc[i][j]);
+                for (int j = 0; j < FB; ++j) acc[i][j] = mfma_16x16x32(a[kk][i], b[kk][j], acc[i][j]);
     };
     auto step = [&](bool more, const uint8_t* xc, const uint8_t* wc, uint8_t* xn, uint8_t* wn_, int64_t kt)
         __attribute__((always_inline)) {
@@ -124,13 +127,13 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     if constexpr (LR) {
         // [TTQ §method b5] low-rank term Y += B (A X) = Z B^T, in fp32, added
         // before the store.  Every DMA has landed and every wave has passed
-        // the last barrier, so the ring slots are free: the tile's Z (256
+        // the last barrier, so the ring slots are free: the tile's Z (BN
         // tokens) and B (128 rows), rank <= 32, are staged there transposed
         // (rank-major), so lanes read consecutive tokens / rows.
-        float* zs = (float*)sX0;                  // [rank][256]
+        float* zs = (float*)sX0;                  // [rank][BN]
         float* bs = (float*)sW0;                  // [rank][128]
-        for (int idx = tid; idx < rank * kBN; idx += kBThreads) {
-            const int k = idx / kBN, tt = idx % kBN;
+        for (int idx = tid; idx < rank * BN; idx += kBThreads) {
+            const int k = idx / BN, tt = idx % BN;
             zs[idx] = (t0 + tt < T) ? Z[(t0 + tt) * rank + k] : 0.0f;
         }
         for (int idx = tid; idx < rank * kBM; idx += kBThreads) {
@@ -139,14 +142,14 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         }
         __syncthreads();
         for (int k = 0; k < rank; ++k) {
-            float zt[4];
+            float zt[FB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zt[j] = zs[k * kBN + wn * 64 + 16 * j + (lane & 15)];
+            for (int j = 0; j < FB; ++j) zt[j] = zs[k * BN + wn * WT + 16 * j + (lane & 15)];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4 bo = *(const f32x4*)(bs + k * kBM + wm * 64 + 16 * i + 4 * (lane >> 4));
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < FB; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(bo[r], zt[j], acc[i][j][r]);
             }
@@ -158,8 +161,8 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     for (int i = 0; i < 4; ++i) {
         const int64_t o = o0 + wm * 64 + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + wn * 64 + 16 * j + (lane & 15);
+        for (int j = 0; j < FB; ++j) {
+            const int64_t t = t0 + wn * WT + 16 * j + (lane & 15);
             if (t >= T) continue;
             store_y4<YF32>(Y, t * ldy + o, M - o, yvec, acc[i][j]);
         }
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
 }
 
 bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw) {
-    return T > 0 && K % kBK == 0 && (int64_t)kBN * ldx * 2 < ((int64_t)1 << 31) &&
+    return T > 0 && K % kBK == 0 && (int64_t)256 * ldx * 2 < ((int64_t)1 << 31) &&
            (int64_t)kBM * ldw * 2 < ((int64_t)1 << 31);
 }
 
@@ -175,19 +178,27 @@ hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
                             StageTimer tm, const LowrankEpilogue* lr) {
     const int yvec = ((uintptr_t)Y % 16 == 0) && ((ldy * (yf32 ? 4 : 2)) % 16 == 0);
-    dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((T + kBN - 1) / kBN));
+    // 128 x 256 tiles, unless they would leave most compute units idle; then
+    // 128 x 128 (twice the workgroups).
+    const int64_t mt = (M + kBM - 1) / kBM;
+    const bool narrow = mt * ((T + 255) / 256) < 192;
+    const dim3 grid((unsigned)mt, (unsigned)((T + (narrow ? 127 : 255)) / (narrow ? 128 : 256)));
     const float* Z = lr ? lr->Z : nullptr;
     const float* B = lr ? lr->B : nullptr;
     const int rank = lr ? lr->rank : 0;
-#define TTQ_B_LAUNCH(YF, LRF)                                                                              \
-    return launch_kernel(k_gemm_bf16<YF, LRF>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, ldx, \
-                         Wq, ldw, M, Y, ldy, yvec, Z, B, rank)
-    if (rank > 0) {
-        if (yf32) TTQ_B_LAUNCH(true, true);
-        TTQ_B_LAUNCH(false, true);
-    }
-    if (yf32) TTQ_B_LAUNCH(true, false);
-    TTQ_B_LAUNCH(false, false);
+#define TTQ_B_LAUNCH(BN, YF, LRF)                                                                          \
+    return launch_kernel(k_gemm_bf16<BN, YF, LRF>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, \
+                         ldx, Wq, ldw, M, Y, ldy, yvec, Z, B, rank)
+#define TTQ_B_LAUNCH2(BN)                                 \
+    if (rank > 0) {                                       \
+        if (yf32) TTQ_B_LAUNCH(BN, true, true);           \
+        TTQ_B_LAUNCH(BN, false, true);                    \
+    }                                                     \
+    if (yf32) TTQ_B_LAUNCH(BN, true, false);              \
+    TTQ_B_LAUNCH(BN, false, false)
+    if (narrow) { TTQ_B_LAUNCH2(128); }
+    TTQ_B_LAUNCH2(256);
+#undef TTQ_B_LAUNCH2
 #undef TTQ_B_LAUNCH
 }
 

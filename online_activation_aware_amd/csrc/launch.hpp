@@ -37,25 +37,20 @@ int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len);
 
 // At most this many fp64 partial rows of K channels in the stats workspace.
 constexpr int kMaxStatsChunks = 32;
-// Optional shrinkage output of the statistics pass: lambda = lambda_rel *
-// mean(ssq / T), finished by the last reduction workgroup.  bsum: ceil(K/64)
-// doubles; done: one counter (zeroed by the pass itself); lam: one double.
-struct StatsLam {
-    float lambda_rel;
-    double* bsum;
-    unsigned* done;
-    double* lam;
-};
+// bsum (optional, ceil(K/64) doubles): per-64-channel block sums of
+// c = ssq / T, from which the quantizer forms lambda = lambda_rel * mean(c).
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st, const StatsLam* lam = nullptr,
+                        int accumulate, double* part, hipStream_t st, double* bsum = nullptr,
                         StageTimer tm = {});
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float* s, hipStream_t st);
 // Scales evaluated inside the quantizer from the statistics (instead of a
-// given s): s[j] = awq_scale(ssq[j], tn, *lam, e), also stored to s_out.
+// given s): lambda = lambda_rel * blocks_total(bsum) / K, then
+// s[j] = awq_scale(ssq[j], tn, lambda, e), also stored to s_out.
 struct QScaleSrc {
     const double* ssq;
-    const double* lam;
+    const double* bsum;
+    double lambda_rel;
     double tn;
     double e;
     float* s_out;

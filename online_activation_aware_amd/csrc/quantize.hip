@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const float* __restrict__ B, const float* __restrict__ A, int rank, int rows_per_block,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero,
     uint16_t* __restrict__ wq, QScaleSrc qs) {
-    extern __shared__ float sA[];                 // [rank][kQChans] when LOWRANK
+    extern __shared__ __attribute__((aligned(16))) float sA[];   // [rank][kQChans] when LOWRANK (16-B reads)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // row addressing stays scalar
@@ -204,6 +204,27 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const bool active = col < K;
     const int64_t cbase = (int64_t)blockIdx.x * kQChans;
 
+    // A row block is WSTRIDE x RB rows: each wave takes RB of them (a batch).
+    // The workgroup walks row blocks rb = blockIdx.y, + gridDim.y, ... (the
+    // grid is sized to the number of workgroups the device holds at once),
+    // and each wave issues the loads of its next batch before it processes
+    // the current one, so loads stay in flight while the VALU works.
+    constexpr int RB = (LOWRANK || WF32) ? 4 : 8;
+    constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
+    const int64_t nrb = (M + rows_per_block - 1) / rows_per_block;
+    auto load_batch = [&](RawRow<WF32> (&dst)[RB], int64_t rb) __attribute__((always_inline)) {
+        const int64_t ob = rb * rows_per_block + wave;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (rb < nrb && active && o < M) {
+                load_row<WF32>(dst[r], W, o, ldw, col);
+            } else {
+                dst[r].a = u32x4{0u, 0u, 0u, 0u};
+                dst[r].b = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
     if constexpr (LOWRANK) {
         for (int idx = threadIdx.x; idx < rank * kQChans; idx += kQThreads) {
             const int k = idx / kQChans, c = idx % kQChans;
@@ -215,9 +236,17 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     // (exactly 1 for s = 1) for the dequantized weight.
     float sc[8], sinv[8];
     if constexpr (SFUSE) {
-        // Each of the strip's 512 scales is evaluated once per workgroup.
+        // lambda from the statistics' block sums (same order as
+        // ttq_awq_scales), then each of the strip's 512 scales once per
+        // workgroup.
         __shared__ float ssc[kQChans];
-        const double lam = *qs.lam;
+        __shared__ double lam_s;
+        if (wave == 0) {
+            const double tot = blocks_total(qs.bsum, (K + 63) / 64, lane);
+            if (lane == 0) lam_s = qs.lambda_rel * (tot / (double)K);
+        }
+        __syncthreads();
+        const double lam = lam_s;
 #pragma unroll
         for (int h = 0; h < kQChans / kQThreads; ++h) {
             const int c = threadIdx.x + h * kQThreads;
@@ -245,27 +274,6 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const int64_t words_per_row = K * BITS / 32;
     const int64_t groups_per_row = K / GROUP;
 
-    // A row block is WSTRIDE x RB rows: each wave takes RB of them (a batch).
-    // The workgroup walks row blocks rb = blockIdx.y, + gridDim.y, ... (the
-    // grid is sized to the number of workgroups the device holds at once),
-    // and each wave issues the loads of its next batch before it processes
-    // the current one, so loads stay in flight while the VALU works.
-    constexpr int RB = (LOWRANK || WF32) ? 4 : 8;
-    constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
-    const int64_t nrb = (M + rows_per_block - 1) / rows_per_block;
-    auto load_batch = [&](RawRow<WF32> (&dst)[RB], int64_t rb) __attribute__((always_inline)) {
-        const int64_t ob = rb * rows_per_block + wave;
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int64_t o = ob + (int64_t)WSTRIDE * r;
-            if (rb < nrb && active && o < M) {
-                load_row<WF32>(dst[r], W, o, ldw, col);
-            } else {
-                dst[r].a = u32x4{0u, 0u, 0u, 0u};
-                dst[r].b = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
     RawRow<WF32> cur[RB];
     load_batch(cur, blockIdx.y);
     for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {

@@ -11,6 +11,9 @@
 
 namespace ttq {
 
+// Channel blocks of 64 for the shrinkage mean: at most 4096 (K <= 2^18).
+constexpr int kMaxBlocks = 4096;
+
 // Wave-wide sum in a fixed butterfly order: every lane receives the same,
 // run-to-run reproducible value.
 __device__ __forceinline__ double wave_sum_fixed(double v) {
@@ -21,11 +24,19 @@ __device__ __forceinline__ double wave_sum_fixed(double v) {
 
 // Channel-block sum of the second moments: block b covers channels
 // 64 b .. 64 b + 63 (lane l <-> channel 64 b + l; missing channels count 0).
-// mean(c) is (sum over blocks, in block order) / K.
 __device__ __forceinline__ double cblock_sum(const double* __restrict__ ssq, int64_t b, int64_t K,
                                              double tn, int lane) {
     const int64_t j = 64 * b + lane;
     return wave_sum_fixed(j < K ? ssq[j] / tn : 0.0);
+}
+
+// Total of the nb block sums in a fixed order (one full wave calls this): lane
+// l adds blocks l, l + 64, ... in order, then the 64 lane totals are combined
+// by wave_sum_fixed.  mean(c) = blocks_total / K.
+__device__ __forceinline__ double blocks_total(const double* bs, int64_t nb, int lane) {
+    double t = 0.0;
+    for (int64_t i = lane; i < nb; i += 64) t += bs[i];
+    return wave_sum_fixed(t);
 }
 
 __device__ __forceinline__ float awq_scale(double ssq_j, double tn, double lam, double e) {

@@ -9,9 +9,8 @@
 // fp32); the 16 waves of a workgroup stride over the rows of one token chunk;
 // squares are accumulated in fp64; the wave partials are combined through LDS
 // in a fixed order and each workgroup writes one fp64 partial row per chunk.
-// k_stats_final sums the chunk partials in chunk order.  Every sum has a
-// fixed order, so results are bitwise reproducible (the one atomic counter
-// only elects the workgroup that finishes the shrinkage mean).
+// k_stats_final sums the chunk partials in a fixed order.  Every sum has a
+// fixed order and there are no atomics, so results are bitwise reproducible.
 #include "common.hpp"
 #include "launch.hpp"
 #include "scales.hpp"
@@ -25,14 +24,12 @@ constexpr int kStatsChans = kWave * 8;      // channels per workgroup strip
 template <bool XF32>
 __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, int rows_per_chunk,
-    double* __restrict__ part, unsigned* __restrict__ done) {
+    double* __restrict__ part) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int64_t c0 = (int64_t)blockIdx.x * kStatsChans + lane * 8;
     const int64_t t0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t t1 = min(T, t0 + rows_per_chunk);
-    // The completion counter of the following reduction starts at zero.
-    if (done != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *done = 0u;
 
     double acc[8];
 #pragma unroll
@@ -86,67 +83,51 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     }
 }
 
-constexpr int kMaxLamBlocks = 4096;          // K <= 2^18
-
-// Sum of the chunk partials, in chunk order: thread <-> channel, 256 channels
-// (four 64-channel blocks) per workgroup.  With LAM, each wave also forms its
-// block's sum of c = ssq / n (cblock_sum order), and the last workgroup to
-// finish adds the block sums in block order and stores
-// lambda = lambda_rel * mean(c) in *lam.
-template <bool LAM>
+// Sum of the chunk partials: a workgroup covers one 64-channel block; its four
+// waves each add a quarter of the chunks (in chunk order, all loads in flight
+// at once) and wave 0 adds the four quarters in order.  With BSUM, wave 0 also
+// stores the block's sum of c = ssq / n (cblock_sum order) in bsum[block];
+// the consumer of lambda totals them after this kernel has finished.
+template <bool BSUM>
 __global__ __launch_bounds__(256) void k_stats_final(const double* __restrict__ part, int nchunks, int64_t K,
                                                      double* __restrict__ ssq, int accumulate, double tn,
-                                                     double lambda_rel, double* __restrict__ bsum,
-                                                     unsigned* __restrict__ done, double* __restrict__ lam) {
+                                                     double* __restrict__ bsum) {
+    __shared__ double red[4][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    double tot = 0.0;
+    const int64_t j = (int64_t)blockIdx.x * kWave + lane;
+    const int per = (nchunks + 3) / 4;
+    const int ch0 = wave * per, ch1 = min(nchunks, ch0 + per);
+    double acc = 0.0;
     if (j < K) {
 #pragma unroll 8
-        for (int ch = 0; ch < nchunks; ++ch) tot += part[(int64_t)ch * K + j];
-        if (accumulate) tot = ssq[j] + tot;
-        ssq[j] = tot;
+        for (int ch = ch0; ch < ch1; ++ch) acc += part[(int64_t)ch * K + j];
     }
-    if constexpr (LAM) {
-        __shared__ bool last;
-        const double bs = wave_sum_fixed(j < K ? tot / tn : 0.0);
-        const int64_t b = (int64_t)blockIdx.x * 4 + wave;
-        if (lane == 0 && 64 * b < K) bsum[b] = bs;
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
-        __syncthreads();
-        if (last) {
-            // Every block sum is written (the other workgroups fenced before
-            // counting); gather them with parallel device-scope loads, then
-            // add them in block order.
-            __threadfence();
-            __shared__ double bl[kMaxLamBlocks];
-            const int64_t nb = (K + 63) / 64;
-            for (int64_t i = threadIdx.x; i < nb; i += 256)
-                bl[i] = __hip_atomic_load(bsum + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                double sum = 0.0;
-                for (int64_t i = 0; i < nb; ++i) sum += bl[i];
-                *lam = lambda_rel * (sum / (double)K);
-            }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        double tot = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        if (j < K) {
+            if (accumulate) tot = ssq[j] + tot;
+            ssq[j] = tot;
+        }
+        if constexpr (BSUM) {
+            const double bs = wave_sum_fixed(j < K ? tot / tn : 0.0);
+            if (lane == 0) bsum[blockIdx.x] = bs;
         }
     }
 }
 
 // Standalone scales from ssq: one workgroup of 1024 threads.  The 16 waves
-// form the 64-channel block sums (cblock_sum) into LDS, thread 0 adds them in
-// block order, then every thread evaluates the scales of its channels.
+// form the 64-channel block sums (cblock_sum) into LDS, wave 0 totals them
+// (blocks_total), then every thread evaluates the scales of its channels.
 constexpr int kScaleThreads = 1024;
-constexpr int kMaxScaleBlocks = 4096;        // K <= 2^18
 
 __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __restrict__ ssq,
                                                               int64_t n_tokens, int64_t K,
                                                               double alpha, double lambda_rel,
                                                               float* __restrict__ s) {
-    __shared__ double bs[kMaxScaleBlocks];
+    __shared__ double bs[kMaxBlocks];
     __shared__ double lam_s;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -157,10 +138,9 @@ __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __re
         if (lane == 0) bs[b] = v;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double sum = 0.0;
-        for (int64_t i = 0; i < nb; ++i) sum += bs[i];
-        lam_s = lambda_rel * (sum / (double)K);
+    if (wave == 0) {
+        const double sum = blocks_total(bs, nb, lane);
+        if (lane == 0) lam_s = lambda_rel * (sum / (double)K);
     }
     __syncthreads();
     const double lam = lam_s, e = alpha / 2.0;
@@ -185,26 +165,24 @@ int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk) {
 }
 
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st, const StatsLam* lam, StageTimer tm) {
+                        int accumulate, double* part, hipStream_t st, double* bsum, StageTimer tm) {
     int rows = 0;
     const int nchunks = stats_chunks(T, K, &rows);
-    unsigned* done = lam ? lam->done : nullptr;
     if (nchunks > 0) {
         dim3 grid((unsigned)((K + kStatsChans - 1) / kStatsChans), (unsigned)nchunks);
         hipError_t e = xf32 ? launch_kernel(k_stats_partial<true>, grid, dim3(kStatsThreads), 0, st, tm.start,
-                                            nullptr, X, T, K, ldx, rows, part, done)
+                                            nullptr, X, T, K, ldx, rows, part)
                             : launch_kernel(k_stats_partial<false>, grid, dim3(kStatsThreads), 0, st, tm.start,
-                                            nullptr, X, T, K, ldx, rows, part, done);
+                                            nullptr, X, T, K, ldx, rows, part);
         if (e != hipSuccess) return e;
     }
-    const dim3 g((unsigned)((K + 255) / 256));
+    const dim3 g((unsigned)((K + kWave - 1) / kWave));
     hipEvent_t e0 = nchunks > 0 ? nullptr : tm.start;
-    if (lam != nullptr)
-        return launch_kernel(k_stats_final<true>, g, dim3(256), 0, st, e0, tm.stop, (const double*)part, nchunks,
-                             K, ssq, accumulate, (double)T, (double)lam->lambda_rel, lam->bsum, lam->done,
-                             lam->lam);
+    if (bsum != nullptr)
+        return launch_kernel(k_stats_final<true>, g, dim3(256), 0, st, e0, tm.stop, (const double*)part, nchunks, K,
+                             ssq, accumulate, (double)T, bsum);
     return launch_kernel(k_stats_final<false>, g, dim3(256), 0, st, e0, tm.stop, (const double*)part, nchunks, K,
-                         ssq, accumulate, 1.0, 0.0, (double*)nullptr, (unsigned*)nullptr, (double*)nullptr);
+                         ssq, accumulate, 1.0, (double*)nullptr);
 }
 
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,

@@ -133,7 +133,7 @@ size_t ws_lowrank(int64_t T, int64_t K, int rank) {
 }
 
 struct StateLayout {
-    size_t ssq, s, codes, scale, zero, bsum, done, lam, scratch, total;
+    size_t ssq, s, codes, scale, zero, bsum, scratch, total;
 };
 StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, int rank) {
     StateLayout L{};
@@ -144,8 +144,6 @@ StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, i
     L.scale = off;   off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
     L.zero = off;    off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
     L.bsum = off;    off += round_up((size_t)((K + 63) / 64) * sizeof(double));
-    L.done = off;    off += kAlign;
-    L.lam = off;     off += kAlign;
     L.scratch = off;
     size_t scratch = ws_stats(T, K);
     // prompt-sized projections: the dequantized weight, then Z = X A^T for
@@ -318,10 +316,10 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                 return e;
         return TTQ_OK;
     };
-    // Statistics; the reduction also finishes lambda = lambda_rel * mean(c).
-    ttq::StatsLam sl{a->lambda_rel, (double*)(w + L.bsum), (unsigned*)(w + L.done), (double*)(w + L.lam)};
+    // Statistics; the reduction also leaves the 64-channel block sums of c.
+    double* bsum = (double*)(w + L.bsum);
     if (ttq_status e = device_status(
-            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st, &sl, timer(0)),
+            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st, bsum, timer(0)),
             "stats"))
         return e;
     if (a->M == 0) {
@@ -335,7 +333,7 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     }
     // The quantizer evaluates the scales of its channels from (ssq, lambda)
     // with the same arithmetic as ttq_awq_scales, and stores s.
-    const ttq::QScaleSrc qs{ssq, sl.lam, (double)a->T, (double)a->alpha / 2.0, s};
+    const ttq::QScaleSrc qs{ssq, bsum, (double)a->lambda_rel, (double)a->T, (double)a->alpha / 2.0, s};
     // Prompt-sized projections: the quantizer also writes the dequantized
     // weight (into the scratch area, free again once the statistics are
     // reduced) and the projection is a plain matrix-core GEMM on it.

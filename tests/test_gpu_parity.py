@@ -192,7 +192,8 @@ def test_qgemm_parity(T, bits, group, K, xdt):
     assert err < (Y_TOL if xdt == "bf16" else 1e-4), err
 
 
-@pytest.mark.parametrize("Tn,M", [(1, 128), (5, 302), (129, 130), (16, 64), (192, 130), (257, 302), (700, 77)])
+@pytest.mark.parametrize("Tn,M", [(1, 128), (5, 302), (129, 130), (16, 64), (192, 130), (257, 302), (700, 77),
+                                  (805, 8142)])   # the last one: 128 x 256 GEMM tiles with ragged T and M
 def test_qgemm_ragged_and_bf16_output(T, Tn, M):
     say(f"qgemm ragged T={Tn} M={M}")
     for ydt, tol in (("f32", Y_TOL), ("bf16", Y_TOL_BF16_OUT)):
