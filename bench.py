@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 # invalidates them (traffic is then reported as null).
 MEASURED_TRAFFIC = {
     # 4096->4096, T=2048 layer: profiles/ttq_linear_4096x4096_t2048_b4g32_pmc_traffic.txt
-    "e396b6d1af2807db": {"workload": "c2", "fetch_bytes": 167930678, "write_bytes": 35468590,
+    "d81c8ec4aef9b073": {"workload": "c2", "fetch_bytes": 167926864, "write_bytes": 34986203,
                          "fetch_factor": 1.9999, "write_factor": 1.0},
 }
 
@@ -262,6 +262,51 @@ def main(argv=None) -> int:
         log(f"  {name:10s} {d['us']:8.2f} us" + (f"  {d['gbs']:8.1f} GB/s" if "gbs" in d else "")
             + (f"  {d['tflops']:8.1f} TFLOP/s" if "tflops" in d else ""))
 
+    # Decode steps (workloads with decode tokens): ttq_qgemm on the prompt's
+    # quantized state for T new tokens, over rotating copies of the state
+    # (cold in the Infinity Cache).  One step per copy is captured in a HIP
+    # graph, so that the figure is the kernels' and not the host's launch rate.
+    decode = None
+    if wl.decode_T:
+        decode = {}
+        sbytes = sum(st[k].numel() * st[k].element_size() for k in ("codes", "scale_f16", "zero_f16"))
+        nst = max(2, min(64, math.ceil((args.min_rotation_mib << 20) / sbytes)))
+        states = [{k: st[k].clone() for k in ("s", "codes", "scale_f16", "zero_f16")} for _ in range(nst)]
+        wsd = ttq.workspace(max(wl.decode_T), wl.K, wl.M, wl.bits, wl.group, device=dev)
+        for td in wl.decode_T:
+            Xd = to_dev(data["X_decode"][td], wl.xdtype)
+            Yd = torch.empty((td, wl.M), dtype=torch.float32, device=dev)
+
+            def dsteps():
+                for q in states:
+                    ttq.ttq_qgemm(Xd, q["s"], q["codes"], q["scale_f16"], q["zero_f16"], wl.M, wl.bits,
+                                  wl.group, Y=Yd, ws=wsd)
+            dsteps()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(graph, stream=side):
+                dsteps()
+            torch.cuda.synchronize()
+            reps = max(1, math.ceil(args.steps / nst))
+            for _ in range(max(1, math.ceil(args.warmup / nst))):
+                graph.replay()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            f0.record()
+            for _ in range(reps):
+                graph.replay()
+            f1.record()
+            torch.cuda.synchronize()
+            us = f0.elapsed_time(f1) / (reps * nst) * 1e3
+            b = sbytes + wl.K * 4 + td * wl.K * esize(wl.xdtype) + td * wl.M * 4
+            decode[str(td)] = {"us": round(us, 2), "alg_bytes": b, "gbs": round(b / (us * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                               "flops": 2 * td * wl.M * wl.K}
+            log(f"  decode T={td:<3d} {us:8.2f} us  {decode[str(td)]['gbs']:8.1f} GB/s "
+                f"({nst} rotating state copies, graph of {nst} steps x {reps})")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same layer ...")
@@ -288,6 +333,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": breakdown,
+        "decode": decode,
     }
     print(json.dumps(out), flush=True)
     return 0
