@@ -124,19 +124,22 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  * [TTQ §method b7] quantized projection kernel; [TTQ §method b1] QDQ:
  * W_hat[o][j] = (code - zero) * step; [TTQ §method b2] inputs divided by s.
  *   Y[t][o] = sum_j W_hat[o][j] * X[t][j] / s[j].
- *   The dequantized weight (code - zero) * step / s[j] is rounded once to
- *   bf16 and multiplied with X on the matrix cores with fp32 accumulation
- *   (bf16 X is used as is; fp32 X is split into two bf16 halves and the
- *   weight too, three products, for near-fp32 accuracy).
+ *   For T >= 5 the dequantized weight (code - zero) * step / s[j] is
+ *   rounded once to bf16 and multiplied with X on the matrix cores with fp32
+ *   accumulation (bf16 X is used as is; fp32 X is split into two bf16 halves
+ *   and the weight too, three products, for near-fp32 accuracy).
  *   X: [T][K] (xt), s: [K], codes/scale/zero as produced by
  *   ttq_quantize_groups for (M, K, bits, group).  Y: [T][M] fp32 or bf16
  *   (yt), overwritten.  Y must not overlap any input.
- *   Three execution paths give the same bf16 weights: for T <= 128 with K a
- *   multiple of 128 (at most 16384) the codes stream straight into registers
- *   and are expanded there (decode steps, short prompts); for bf16 X with
- *   T >= 192 and K a multiple of 64 the weight is dequantized once into ws
- *   (M*K bf16) and multiplied by a matrix-core GEMM; otherwise codes are
- *   dequantized tile by tile inside the GEMM kernel.
+ *   Execution paths: for T <= 4 with K a multiple of 128 (decode steps) the
+ *   vector ALUs compute step * (sum code * x/s - zero * sum x/s) per group
+ *   in fp32, with no bf16 rounding; for 5 <= T <= 128 with K a multiple of
+ *   128 (at most 16384) the codes stream straight into registers and are
+ *   expanded there to the bf16 weights above; for bf16 X with T >= 192 and
+ *   K a multiple of 64 the weight is dequantized once into ws (M*K bf16) and
+ *   multiplied by a matrix-core GEMM; otherwise codes are dequantized tile
+ *   by tile inside the GEMM kernel.  The last three see bitwise the same
+ *   bf16 weights.
  *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (M*K*2
  *   rounded up to 256 when T >= 192, none otherwise); only read and written
  *   by the kernels this call enqueues.

@@ -203,17 +203,275 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
     }
 }
 
-// Token rows up to 127 are addressed (padded tiles read as zero) with 32-bit
-// buffer offsets.
+// ---------------------------------------------------------------------------
+// One to four tokens: the vector ALUs, with the group affine map applied to
+// sums instead of to weights.
+//
+// For a group h of row o, sum_k (q_k - z_h) * step_h * xs_k
+//   = step_h * (sum_k q_k * xs_k - z_h * sum_k xs_k),     xs = x / s,
+// and sum_k xs_k does not depend on o.  A lane therefore converts each code
+// to fp32 once (v_cvt_f32_ubyteN on masked nibbles for b = 4) and does one
+// FMA per code and token; the step and zero cost two FMAs per group.  xs is
+// formed once per wave in fp32 (x * v_rcp(s)), so the only rounding is fp32
+// accumulation: no bf16 rounding of weights or tokens on this path.
+//
+// Mapping: a piece is 64 lanes x 32 consecutive channels (2048 channels;
+// b x 256 bytes of codes per row).  A workgroup owns RW rows; its NS waves
+// take the pieces w, w + NS, ...; per piece a wave issues the codes of all
+// RW rows (one contiguous 16-byte load per lane and row at b = 4) before it
+// computes, so each load instruction reads a contiguous b x 256-byte run of
+// one row.  Per-lane sums are added over the wave by a fixed butterfly and
+// over the waves in wave order (deterministic).
+constexpr int kTChan = 32;                        // channels per lane
+constexpr int kTPiece = kTChan * kWave;           // channels per piece
+constexpr int kTMaxWaves = 8;
+constexpr int trows(int tt) { return tt == 4 ? 8 : 16; }   // rows per workgroup
+constexpr int tdepth(int tt) { return tt == 4 ? 2 : tt == 2 ? 4 : 8; }   // rows in flight per wave
+
+template <int N>
+__device__ __forceinline__ float cvt_ubyte(uint32_t v) {
+    float f;
+    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+    return f;
+}
+
+// The 32 codes of a lane's field as fp32 values, code i at bits BITS*i of the
+// little-endian bit stream.
+template <int BITS>
+__device__ __forceinline__ void field_codes(const CodeWords<BITS>& c, float (&q)[kTChan]) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = c.w[i] & 0x0F0F0F0Fu, hi = (c.w[i] >> 4) & 0x0F0F0F0Fu;
+            q[8 * i + 0] = cvt_ubyte<0>(lo);
+            q[8 * i + 1] = cvt_ubyte<0>(hi);
+            q[8 * i + 2] = cvt_ubyte<1>(lo);
+            q[8 * i + 3] = cvt_ubyte<1>(hi);
+            q[8 * i + 4] = cvt_ubyte<2>(lo);
+            q[8 * i + 5] = cvt_ubyte<2>(hi);
+            q[8 * i + 6] = cvt_ubyte<3>(lo);
+            q[8 * i + 7] = cvt_ubyte<3>(hi);
+        }
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t m = (c.w[i] >> (2 * j)) & 0x03030303u;   // codes 4 b + j of this word
+                q[16 * i + j] = cvt_ubyte<0>(m);
+                q[16 * i + 4 + j] = cvt_ubyte<1>(m);
+                q[16 * i + 8 + j] = cvt_ubyte<2>(m);
+                q[16 * i + 12 + j] = cvt_ubyte<3>(m);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTChan; ++i) q[i] = (float)code_at<BITS>(c, i);
+    }
+}
+
+template <int BITS, int SG>
+struct RowField {
+    CodeWords<BITS> cw;
+    uint16_t dh[SG], zh[SG];
+};
+
+template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
+__global__ __launch_bounds__(kTMaxWaves * kWave) void k_qgemv_t(
+    const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint16_t* __restrict__ zero, int64_t M, void* __restrict__ Y, int64_t ldy) {
+    constexpr int RW = trows(TT);
+    constexpr int D = tdepth(TT);
+    constexpr int SG = GROUP < kTChan ? kTChan / GROUP : 1;   // groups per lane field
+    constexpr int SGC = kTChan / SG;                          // channels per group part
+    constexpr int NV = RW * TT;
+    __shared__ float red[kTMaxWaves][NV];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int NS = blockDim.x / kWave;
+    const int64_t o0 = (int64_t)blockIdx.x * RW;
+    const int64_t wpr = K * BITS / 32, gpr = K / GROUP;
+    const int64_t npieces = (K + kTPiece - 1) / kTPiece;
+
+    float acc[RW][TT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
+
+    for (int64_t p = wave; p < npieces; p += NS) {
+        const int64_t k0 = p * kTPiece + (int64_t)lane * kTChan;
+        if (k0 < K) {                             // K % 32 == 0: a field is all in or all out
+            auto load_row = [&](RowField<BITS, SG>& f, int r) __attribute__((always_inline)) {
+                const int64_t o = o0 + r < M ? o0 + r : M - 1;
+                load_codes<BITS>(f.cw, codes + o * wpr + k0 * BITS / 32);
+#pragma unroll
+                for (int h = 0; h < SG; ++h) {
+                    f.dh[h] = scale[o * gpr + k0 / GROUP + h];
+                    f.zh[h] = zero[o * gpr + k0 / GROUP + h];
+                }
+            };
+            // Requests in the order they are waited for (the vector memory
+            // counter drains in order): scales and tokens of this field, then
+            // the first D rows.  fp32 tokens with four token slots are fetched
+            // after the rows, one token at a time, to bound registers.
+            constexpr bool kEarlyX = !(XF32 && TT == 4);
+            constexpr int XW = XF32 ? kTChan : kTChan / 2;     // 32-bit words per token field
+            float sv[kTChan];
+#pragma unroll
+            for (int v = 0; v < kTChan / 4; ++v) {
+                const f32x4 a = *(const f32x4*)(s + k0 + 4 * v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[4 * v + e] = a[e];
+            }
+            auto load_x = [&](uint32_t (&xr)[XW], int t) __attribute__((always_inline)) {
+                const u32x4* xp = XF32 ? (const u32x4*)((const float*)X + t * ldx + k0)
+                                       : (const u32x4*)((const uint16_t*)X + t * ldx + k0);
+#pragma unroll
+                for (int v = 0; v < XW / 4; ++v) {
+                    const u32x4 a = t < T ? xp[v] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xr[4 * v + e] = a[e];
+                }
+            };
+            uint32_t xr[kEarlyX ? TT : 1][XW];
+            if constexpr (kEarlyX) {
+#pragma unroll
+                for (int t = 0; t < TT; ++t) load_x(xr[t], t);
+            }
+            RowField<BITS, SG> ring[D];
+#pragma unroll
+            for (int r = 0; r < D; ++r) load_row(ring[r], r);
+            __builtin_amdgcn_sched_barrier(0);              // all D rows requested before any wait
+
+            // xs = x * (1/s) and its sums over each group part.
+#pragma unroll
+            for (int i = 0; i < kTChan; ++i) sv[i] = __builtin_amdgcn_rcpf(sv[i]);
+            float xs[TT][kTChan], S[TT][SG];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                if constexpr (!kEarlyX) load_x(xr[0], t);
+                const uint32_t(&xt)[XW] = xr[kEarlyX ? t : 0];
+#pragma unroll
+                for (int i = 0; i < kTChan; ++i) {
+                    float x;
+                    if constexpr (XF32) x = __builtin_bit_cast(float, xt[i]);
+                    else x = (i & 1) ? bf16hi_to_f32(xt[i / 2]) : bf16lo_to_f32(xt[i / 2]);
+                    xs[t][i] = x * sv[i];
+                }
+#pragma unroll
+                for (int h = 0; h < SG; ++h) {
+                    float a = xs[t][h * SGC];
+#pragma unroll
+                    for (int i = 1; i < SGC; ++i) a += xs[t][h * SGC + i];
+                    S[t][h] = a;
+                }
+            }
+
+            // Rows stream through a ring of D fields: row r + D is requested
+            // before row r is computed.
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const RowField<BITS, SG> f = ring[r % D];
+                if (r + D < RW) load_row(ring[r % D], r + D);
+                float q[kTChan];
+                field_codes<BITS>(f.cw, q);
+#pragma unroll
+                for (int h = 0; h < SG; ++h) {
+                    const float df = f16_to_f32(f.dh[h]), zf = f16_to_f32(f.zh[h]);
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        float d = q[h * SGC] * xs[t][h * SGC];
+#pragma unroll
+                        for (int i = 1; i < SGC; ++i) d = __builtin_fmaf(q[h * SGC + i], xs[t][h * SGC + i], d);
+                        acc[r][t] = __builtin_fmaf(df, __builtin_fmaf(-zf, S[t][h], d), acc[r][t]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);          // rows are not interleaved (registers)
+            }
+        }
+    }
+
+    // Sum over the wave: at each butterfly step a lane keeps half of its
+    // values and adds its partner's copy of them; afterwards lane l holds the
+    // wave total of value idx(l), whose bits are lane bits 5, 4, ... .
+    float v[NV];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) v[r * TT + t] = acc[r][t];
+    int n = NV, idx = 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        if (n > 1) {
+            const int half = n / 2;
+            const bool up = (lane & m) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                // Selects written on the bit patterns: a per-lane choice between
+                // two array elements must not become a dynamic array index.
+                const uint32_t a = __builtin_bit_cast(uint32_t, v[i]);
+                const uint32_t b = __builtin_bit_cast(uint32_t, v[i + half]);
+                const uint32_t um = up ? 0xFFFFFFFFu : 0u;
+                const float send = __builtin_bit_cast(float, (a & um) | (b & ~um));
+                const float keep = __builtin_bit_cast(float, (b & um) | (a & ~um));
+                v[i] = keep + __shfl_xor(send, m);
+            }
+            idx = 2 * idx + (up ? 1 : 0);
+            n = half;
+        } else {
+            v[0] += __shfl_xor(v[0], m);
+        }
+    }
+    constexpr int kLowBits = 6 - __builtin_ctz(NV);            // lane bits below the index bits
+    if ((lane & ((1 << kLowBits) - 1)) == 0) red[wave][idx] = v[0];
+    __syncthreads();
+    if (threadIdx.x < NV) {
+        const int vi = threadIdx.x;
+        float a = red[0][vi];
+        for (int w = 1; w < NS; ++w) a += red[w][vi];
+        const int r = vi / TT, t = vi % TT;
+        const int64_t o = o0 + r;
+        if (o < M && t < T) {
+            if constexpr (YF32) ((float*)Y)[t * ldy + o] = a;
+            else ((uint16_t*)Y)[t * ldy + o] = (uint16_t)f32_to_bf16(a);
+        }
+    }
+}
+
+template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
+static hipError_t launch_t(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
+                           const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, void* Y,
+                           int64_t ldy, hipStream_t st, StageTimer tm) {
+    const int64_t np = (K + kTPiece - 1) / kTPiece;
+    const int64_t rounds = (np + kTMaxWaves - 1) / kTMaxWaves;
+    const int ns = (int)((np + rounds - 1) / rounds);           // waves, each taking `rounds` pieces
+    const dim3 grid((unsigned)((M + trows(TT) - 1) / trows(TT)));
+    return launch_kernel(k_qgemv_t<BITS, GROUP, XF32, YF32, TT>, grid, dim3(ns * kWave), 0, st, tm.start, tm.stop,
+                         X, T, K, ldx, s, codes, scale, zero, M, Y, ldy);
+}
+
+// T <= 4 runs k_qgemv_t (64-bit addressing, any K).  Above that, token rows
+// up to 127 are addressed (padded tiles read as zero) with 32-bit buffer
+// offsets, and 1/s of every channel is staged in LDS.
 bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32) {
-    return T >= 1 && T <= kQgemvMaxT && K % kVChunk == 0 && K <= kVMaxK &&
-           (int64_t)kQgemvMaxT * ldx * (xf32 ? 4 : 2) < ((int64_t)1 << 31);
+    if (T < 1 || T > kQgemvMaxT || K % kVChunk != 0) return false;
+    if (T <= 4) return true;
+    return K <= kVMaxK && (int64_t)kQgemvMaxT * ldx * (xf32 ? 4 : 2) < ((int64_t)1 << 31);
 }
 
 template <int BITS, int GROUP, bool XF32, bool YF32>
 static hipError_t launch_v4(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
                             const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M,
                             void* Y, int64_t ldy, hipStream_t st, StageTimer tm) {
+    if (T == 1) return launch_t<BITS, GROUP, XF32, YF32, 1>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
+    if (T == 2) return launch_t<BITS, GROUP, XF32, YF32, 2>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
+    if (T <= 4) return launch_t<BITS, GROUP, XF32, YF32, 4>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
     const dim3 grid((unsigned)((M + 15) / 16));
 #define TTQ_V_LAUNCH(NT)                                                                                  \
     return launch_kernel(k_qgemv<BITS, GROUP, XF32, YF32, NT>, grid, dim3(vwaves(NT) * kWave), 0, st,     \

@@ -214,6 +214,22 @@ def test_qgemv_parity(T, Tn, bits, group):
         assert err < (Y_TOL if xdt == "bf16" else 1e-4), (xdt, err)
 
 
+@pytest.mark.parametrize("Tn", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits,group,K", [(4, 32, 1152), (4, 32, 4224), (3, 16, 4224), (2, 64, 18432),
+                                          (5, 128, 4224), (4, 16, 2048), (2, 128, 1152)])
+def test_qgemv_few_tokens(T, Tn, bits, group, K):
+    # One to four tokens run on the vector ALUs in fp32 (no bf16 rounding of
+    # weights or tokens), so the bar is fp32 accumulation, not 2e-3.  K = 1152
+    # and 4224 end in a partial 2048-channel piece; K = 18432 gives 9 pieces
+    # over 5 waves; M = 203 a partial 8-row block.
+    say(f"qgemv few tokens T={Tn} bits={bits} group={group} K={K}")
+    for xdt in ("bf16", "f32"):
+        key = "c1" if xdt == "f32" else "c2"
+        got, ref = _qgemm_case(T, key, Tn, K, 203, bits, group, xdt, "f32", seed=Tn + 7 * bits)
+        err = rel_fro(got, ref)
+        assert err < 2e-5, (xdt, err)
+
+
 def test_qgemm_identity_input_layout(T):
     # X = I: Y[t][o] = bf16((q - z) * step / s_t), element by element.
     say("qgemm identity layout")
