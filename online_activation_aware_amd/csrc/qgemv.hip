@@ -226,7 +226,7 @@ constexpr int kTChan = 32;                        // channels per lane
 constexpr int kTPiece = kTChan * kWave;           // channels per piece
 constexpr int kTMaxWaves = 8;
 constexpr int trows(int tt) { return tt == 4 ? 8 : 16; }   // rows per workgroup
-constexpr int tdepth(int tt) { return tt == 4 ? 2 : tt == 2 ? 4 : 8; }   // rows in flight per wave
+constexpr int tdepth(int tt) { return tt == 1 ? 3 : 2; }                  // rows in flight per wave
 
 template <int N>
 __device__ __forceinline__ float cvt_ubyte(uint32_t v) {
