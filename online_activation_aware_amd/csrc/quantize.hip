@@ -280,36 +280,60 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
         RawRow<WF32> nxt[RB];
         load_batch(nxt, rb + gridDim.y);
         const int64_t ob = rb * rows_per_block + wave;
+        if constexpr (LOWRANK) {
+            // Residual of the batch's RB rows, rank-ordered fp64 sums per
+            // element: each A value is read from LDS and widened once per
+            // batch and used for all RB rows.
+            double acc[RB][8];
+            const float* Brow[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int64_t o = ob + (int64_t)WSTRIDE * r;
-            if (o >= M) break;                    // wave-uniform
-            float wv[8];
-            unpack_row<WF32>(cur[r], wv);
-            float v[8];
-            if constexpr (LOWRANK) {
-                double acc[8];
+            for (int r = 0; r < RB; ++r) {
+                float wv[8];
+                unpack_row<WF32>(cur[r], wv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = (double)wv[i];
-                const float* Brow = B + o * rank;
-                for (int k = 0; k < rank; ++k) {
-                    const double nb = -(double)Brow[k];
-                    const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
-                    f32x4 a0 = ak[0], a1 = ak[1];
+                for (int i = 0; i < 8; ++i) acc[r][i] = (double)wv[i];
+                const int64_t o = ob + (int64_t)WSTRIDE * r;
+                Brow[r] = B + (o < M ? o : M - 1) * rank;
+            }
+            for (int k = 0; k < rank; ++k) {
+                const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
+                const f32x4 a0 = ak[0], a1 = ak[1];
+                double ad[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[i] = __builtin_fma(nb, (double)a0[i], acc[i]);
-                        acc[4 + i] = __builtin_fma(nb, (double)a1[i], acc[4 + i]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    ad[i] = (double)a0[i];
+                    ad[4 + i] = (double)a1[i];
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[i] * (double)sc[i]);
-            } else {
+                for (int r = 0; r < RB; ++r) {
+                    const double nb = -(double)Brow[r][k];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[r][i] = __builtin_fma(nb, ad[i], acc[r][i]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int64_t o = ob + (int64_t)WSTRIDE * r;
+                if (o >= M) break;                // wave-uniform
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[r][i] * (double)sc[i]);
+                quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
+                                                codes, scale, zero, sinv, wq, K);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int64_t o = ob + (int64_t)WSTRIDE * r;
+                if (o >= M) break;                // wave-uniform
+                float wv[8];
+                unpack_row<WF32>(cur[r], wv);
+                float v[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) v[i] = wv[i] * sc[i];
+                quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
+                                                codes, scale, zero, sinv, wq, K);
             }
-            quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
-                                            codes, scale, zero, sinv, wq, K);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) cur[r] = nxt[r];
