@@ -27,8 +27,9 @@ Readings where the page is silent (each listed in the design notes):
   * diagonal covariance = uncentered per-channel mean of squares over the
     prompt's tokens (the loss in b3 expands with E[X X^T]);
   * shrinkage = ridge: C + lambda I, lambda = lambda_rel * mean_j(c_j);
-  * p = moment order of the per-channel magnitude, p = 2 only:
-    s_j = (c_j + lambda)^(alpha/2); s_j = 1 where c_j + lambda == 0;
+  * p = moment order of the per-channel magnitude: c_j = mean_t |x_tj|^p
+    (p = 2: the diagonal covariance; p = 1: mean |x|, AWQ's own statistic),
+    s_j = (c_j + lambda)^(alpha/p); s_j = 1 where c_j + lambda == 0;
   * group = g consecutive input channels of one output row;
   * asymmetric RTN with a 0-extended range and an integer zero point;
     the step is stored as fp16 rounded toward +inf (so the grid covers the
@@ -69,16 +70,26 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
 
 # --------------------------------------------------------------- statistics
 
-def stats(X: np.ndarray, xdtype: str, ssq_prev: np.ndarray | None = None) -> np.ndarray:
-    """Per-channel sum of squares of the prompt activations, fp64.
+def stats(X: np.ndarray, xdtype: str, ssq_prev: np.ndarray | None = None,
+          p: float = 2.0) -> np.ndarray:
+    """Per-channel sum of |x|^p of the prompt activations, fp64.
 
     [TTQ §method b2, b3]: the activation statistics that the closed form uses
     are the diagonal of the input covariance; here ssq_j = sum_t x_tj^2 (the
-    division by the token count happens in `awq_scales`).  ``ssq_prev`` adds
-    the sums of earlier chunks of the same prompt.
+    division by the token count happens in `awq_scales`).  [TTQ §method b4]
+    fixes p in advance; for p != 2 the statistic is the p-th absolute moment
+    sum, sum_t |x_tj|^p (p arrives as an fp32 number, widened exactly).
+    ``ssq_prev`` adds the sums of earlier chunks of the same prompt.
     """
     x = decode(X, xdtype)
-    ssq = np.sum(x * x, axis=0, dtype=np.float64)
+    pp = float(np.float32(p))
+    if pp == 2.0:
+        m = x * x
+    elif pp == 1.0:
+        m = np.abs(x)
+    else:
+        m = np.power(np.abs(x), pp)
+    ssq = np.sum(m, axis=0, dtype=np.float64)
     if ssq_prev is not None:
         ssq = np.asarray(ssq_prev, dtype=np.float64) + ssq
     return ssq
@@ -91,12 +102,13 @@ def awq_scales(ssq: np.ndarray, n_tokens: int, alpha: float, lambda_rel: float,
     [TTQ §method b2-b4]: c_j = ssq_j / T is the diagonal covariance estimate;
     the shrunk estimate is c_j + lambda with lambda = lambda_rel * mean(c);
     the AWQ scale is the channel magnitude raised to the fixed alpha, here
-    s_j = (c_j + lambda)^(alpha/p) with p = 2, evaluated in fp64 and rounded
-    once to fp32.  alpha, lambda_rel and p arrive as fp32 numbers and are
-    widened exactly.  Where c_j + lambda == 0 the scale is defined as 1.
+    s_j = (c_j + lambda)^(alpha/p), where ssq holds the p-th moment sums of
+    `stats` with the same p (p = 2: sums of squares), evaluated in fp64 and
+    rounded once to fp32.  alpha, lambda_rel and p arrive as fp32 numbers and
+    are widened exactly.  Where c_j + lambda == 0 the scale is defined as 1.
     """
-    if float(np.float32(p)) != 2.0:
-        raise NotImplementedError("only p = 2 (second-moment magnitude) is defined")
+    if not (np.isfinite(np.float32(p)) and float(np.float32(p)) > 0.0):
+        raise ValueError("p must be finite and > 0")
     ssq = np.asarray(ssq, dtype=np.float64)
     K = ssq.shape[0]
     c = ssq / np.float64(n_tokens)
@@ -290,7 +302,7 @@ def linear(X, xdtype, W, wdtype, bits, group, alpha, lambda_rel, p=2.0,
     ``rows`` restricts the quantization and the projection to a subset of
     output rows (for sampled checks at full size)."""
     T = np.asarray(X).shape[0]
-    ssq = stats(X, xdtype)
+    ssq = stats(X, xdtype, p=p)
     s = awq_scales(ssq, T, alpha, lambda_rel, p)
     Wr = W if rows is None else np.asarray(W)[rows]
     Br = None if B is None else (B if rows is None else np.asarray(B)[rows])

@@ -10,6 +10,7 @@ the TTQ review page; "[TTQ §results rN]" = bullet N of its key-results section.
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -98,9 +99,57 @@ def test_scales_monotone_and_power_law():
         np.testing.assert_allclose(s2, s1 * 2.0 ** alpha, rtol=2e-7)
 
 
-def test_scales_p_other_than_two_rejected():
-    with pytest.raises(NotImplementedError):
-        oracle.awq_scales(np.ones(4), 1, 0.5, 1e-2, p=1.0)
+# p-th moment statistics ([TTQ §method b4]: p fixed in advance).
+
+@pytest.mark.parametrize("p", [2.0, 1.0, 3.0, 0.5])
+def test_stats_p_moment_equals_library_norm(p):
+    # sum_t |x_tj|^p is the p-th power of the column's l_p norm: torch's
+    # vector_norm is an independent evaluation of it.
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((57, 40)) * rng.lognormal(0, 1, 40)).astype(np.float32)
+    got = oracle.stats(x, "f32", p=p)
+    ref = torch.linalg.vector_norm(torch.from_numpy(x.astype(np.float64)), ord=p, dim=0).numpy() ** p
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+def test_scales_p_constant_magnitude_gives_same_scale():
+    # Channels whose |x| is constant a: mean |x|^p = a^p for every p, so with
+    # lambda = 0, s = (a^p)^(alpha/p) = a^alpha whatever p is (the equality
+    # case of the power-mean inequality).
+    rng = np.random.default_rng(32)
+    a = np.array([4.0, 0.25, 9.0, 1.0])
+    x = (np.where(rng.random((16, 4)) < 0.5, -1.0, 1.0) * a).astype(np.float32)
+    for p in (0.5, 1.0, 2.0, 3.0):
+        s = oracle.awq_scales(oracle.stats(x, "f32", p=p), 16, 0.5, 0.0, p=p).astype(np.float64)
+        np.testing.assert_allclose(s, np.sqrt(a), rtol=2e-7)
+
+
+def test_scales_p_power_mean_order():
+    # With lambda = 0, s_j = M_p(x_j)^alpha where M_p is the power mean of
+    # |x_tj|; M_p grows with p, strictly unless |x| is constant over t.
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal((64, 50)) * rng.lognormal(0, 1, 50)).astype(np.float32)
+    sp = [oracle.awq_scales(oracle.stats(x, "f32", p=p), 64, 0.5, 0.0, p=p).astype(np.float64)
+          for p in (0.5, 1.0, 2.0, 4.0)]
+    for lo, hi in zip(sp, sp[1:]):
+        assert np.all(lo < hi)
+
+
+@pytest.mark.parametrize("p", [0.5, 1.0, 3.0])
+def test_scales_p_homogeneous_of_degree_alpha(p):
+    # X -> 4X multiplies every |x|^p, c and lambda by 4^p, hence s by 4^alpha.
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((20, 64)).astype(np.float32)
+    for alpha in (0.5, 0.25):
+        s1 = oracle.awq_scales(oracle.stats(x, "f32", p=p), 20, alpha, 1e-2, p=p).astype(np.float64)
+        s4 = oracle.awq_scales(oracle.stats(4.0 * x, "f32", p=p), 20, alpha, 1e-2, p=p).astype(np.float64)
+        np.testing.assert_allclose(s4, s1 * 4.0 ** alpha, rtol=2e-7)
+
+
+def test_scales_p_must_be_positive():
+    for p in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            oracle.awq_scales(np.ones(4), 1, 0.5, 1e-2, p=p)
 
 
 # ----------------------------------------------------------- quantization
