@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
     TTQ_OK = 0,
     TTQ_ERR_INVALID = 1,      /* malformed arguments: nothing launched      */
-    TTQ_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (p != 2)   */
+    TTQ_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented            */
     TTQ_ERR_DEVICE = 3        /* the HIP runtime refused a launch           */
 } ttq_status;
 
@@ -82,14 +82,29 @@ ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
                      void* stream);
 
 /*
+ * ttq_stats_p — per-channel sum of |x|^p, for a moment order p fixed in
+ * advance.  [TTQ §method b4]: alpha, lambda and p are fixed, not searched;
+ * p = 2 is the diagonal covariance of ttq_stats, p = 1 the mean absolute
+ * activation of the original AWQ statistic.
+ *   msum[j] (+)= sum_{t<T} |X[t][j]|^p in fp64: exact squares for p = 2,
+ *   exact |x| for p = 1, fp64 pow(|x|, p) otherwise (0 for x = 0).
+ *   p finite and > 0 (else TTQ_ERR_INVALID).  Everything else (X, msum,
+ *   accumulate, ws, ordering and reproducibility) is as for ttq_stats, which
+ *   is this call with p = 2.  Feed msum to ttq_awq_scales with the same p.
+ */
+ttq_status ttq_stats_p(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
+                       float p, double* msum, int accumulate, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
  * ttq_awq_scales — shrunk AWQ per-channel scales.
  * [TTQ §method b2-b4]: c = ssq / n_tokens; lambda = lambda_rel * mean(c)
  * (shrinkage C + lambda I); s[j] = (c[j] + lambda)^(alpha / p), evaluated in
  * fp64 and rounded once to fp32; s[j] = 1 where c[j] + lambda == 0.
  * alpha, lambda_rel, p are fixed in advance (no search).
- *   ssq: [K] fp64 input.  s: [K] fp32 output.  n_tokens > 0.
- *   alpha and lambda_rel finite and >= 0.  p must be 2 (second moment), any
- *   other value returns TTQ_ERR_UNSUPPORTED.
+ *   ssq: [K] fp64 input, the sums of |x|^p from ttq_stats_p with the same p
+ *   (sums of squares for p = 2).  s: [K] fp32 output.  n_tokens > 0.
+ *   alpha and lambda_rel finite and >= 0; p finite and > 0.
  */
 ttq_status ttq_awq_scales(const double* ssq, int64_t n_tokens, int64_t K,
                           float alpha, float lambda_rel, float p, float* s,
@@ -173,9 +188,10 @@ size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group,
 
 /*
  * ttq_linear — the whole per-prompt path of one linear layer.
- * [TTQ §method b1-b5, b7]: statistics of this prompt's X -> shrunk AWQ
- * scales -> group RTN of (W - B A) diag(s) -> quantized projection, plus
- * B (A X) when rank > 0.  Equivalent to the five calls above in order.
+ * [TTQ §method b1-b5, b7]: statistics of this prompt's X (sums of |x|^p,
+ * ttq_stats_p) -> shrunk AWQ scales with the same p -> group RTN of
+ * (W - B A) diag(s) -> quantized projection, plus B (A X) when rank > 0.
+ * Equivalent to the five calls above in order.
  * The optional outputs (ssq, s, codes, scale_f16, zero_f16) receive the
  * prompt's quantization state so that later decode steps can call ttq_qgemm
  * on it; when NULL they live in the workspace.

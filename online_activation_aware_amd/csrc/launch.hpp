@@ -39,11 +39,12 @@ int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len);
 constexpr int kMaxStatsChunks = 32;
 // bsum (optional, ceil(K/64) doubles): per-64-channel block sums of
 // c = ssq / T, from which the quantizer forms lambda = lambda_rel * mean(c).
+// p: moment order of the statistic, sum |x|^p (2: sums of squares).
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
                         int accumulate, double* part, hipStream_t st, double* bsum = nullptr,
-                        StageTimer tm = {});
+                        StageTimer tm = {}, double p = 2.0);
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
-                             float lambda_rel, float* s, hipStream_t st);
+                             float lambda_rel, float p, float* s, hipStream_t st);
 // Scales evaluated inside the quantizer from the statistics (instead of a
 // given s): lambda = lambda_rel * blocks_total(bsum) / K, then
 // s[j] = awq_scale(ssq[j], tn, lambda, e), also stored to s_out.

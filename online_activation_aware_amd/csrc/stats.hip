@@ -7,8 +7,9 @@
 // k_stats_partial: a coalesced column reduction.  Each lane owns 8
 // consecutive channels (one 16-byte bf16 load per token row, or two for
 // fp32); the 16 waves of a workgroup stride over the rows of one token chunk;
-// squares are accumulated in fp64; the wave partials are combined through LDS
-// in a fixed order and each workgroup writes one fp64 partial row per chunk.
+// squares (or, for a moment order p != 2 [TTQ §method b4], |x|^p) are
+// accumulated in fp64; the wave partials are combined through LDS in a fixed
+// order and each workgroup writes one fp64 partial row per chunk.
 // k_stats_final sums the chunk partials in a fixed order.  Every sum has a
 // fixed order and there are no atomics, so results are bitwise reproducible.
 #include "common.hpp"
@@ -21,10 +22,19 @@ constexpr int kStatsThreads = 1024;         // 16 waves: all of a chunk's rows i
 constexpr int kStatsWaves = kStatsThreads / kWave;
 constexpr int kStatsChans = kWave * 8;      // channels per workgroup strip
 
-template <bool XF32>
+// |x|^p added to acc in fp64: PM = 2 squares (exact products), PM = 1 absolute
+// values, PM = 0 any other p (fp64 pow of |x|; 0 for x = 0).
+template <int PM>
+__device__ __forceinline__ double add_moment(double x, double p, double acc) {
+    if constexpr (PM == 2) return __builtin_fma(x, x, acc);
+    else if constexpr (PM == 1) return acc + __builtin_fabs(x);
+    else return acc + (x == 0.0 ? 0.0 : pow(__builtin_fabs(x), p));
+}
+
+template <bool XF32, int PM>
 __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, int rows_per_chunk,
-    double* __restrict__ part) {
+    double* __restrict__ part, double pexp) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int64_t c0 = (int64_t)blockIdx.x * kStatsChans + lane * 8;
@@ -44,10 +54,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
                 f32x4 a = ld_nc(p), b = ld_nc(p + 1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    double x = (double)a[i];
-                    acc[i] = __builtin_fma(x, x, acc[i]);
-                    double y = (double)b[i];
-                    acc[4 + i] = __builtin_fma(y, y, acc[4 + i]);
+                    acc[i] = add_moment<PM>((double)a[i], pexp, acc[i]);
+                    acc[4 + i] = add_moment<PM>((double)b[i], pexp, acc[4 + i]);
                 }
             }
         } else {
@@ -57,10 +65,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats_partial(
                 u32x4 w = ld_nc((const u32x4*)(base + t * ldx));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    double x = (double)bf16lo_to_f32(w[i]);
-                    acc[2 * i] = __builtin_fma(x, x, acc[2 * i]);
-                    double y = (double)bf16hi_to_f32(w[i]);
-                    acc[2 * i + 1] = __builtin_fma(y, y, acc[2 * i + 1]);
+                    acc[2 * i] = add_moment<PM>((double)bf16lo_to_f32(w[i]), pexp, acc[2 * i]);
+                    acc[2 * i + 1] = add_moment<PM>((double)bf16hi_to_f32(w[i]), pexp, acc[2 * i + 1]);
                 }
             }
         }
@@ -125,7 +131,7 @@ constexpr int kScaleThreads = 1024;
 
 __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __restrict__ ssq,
                                                               int64_t n_tokens, int64_t K,
-                                                              double alpha, double lambda_rel,
+                                                              double e, double lambda_rel,
                                                               float* __restrict__ s) {
     __shared__ double bs[kMaxBlocks];
     __shared__ double lam_s;
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kScaleThreads) void k_awq_scales(const double* __re
         if (lane == 0) lam_s = lambda_rel * (sum / (double)K);
     }
     __syncthreads();
-    const double lam = lam_s, e = alpha / 2.0;
+    const double lam = lam_s;
     for (int64_t j = threadIdx.x; j < K; j += kScaleThreads) s[j] = awq_scale(ssq[j], tn, lam, e);
 }
 
@@ -164,16 +170,27 @@ int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk) {
     return T > 0 ? (int)((T + rows - 1) / rows) : 0;
 }
 
+template <bool XF32>
+static hipError_t launch_partial(dim3 grid, const void* X, int64_t T, int64_t K, int64_t ldx, int rows,
+                                 double* part, double p, hipStream_t st, hipEvent_t e0) {
+    if (p == 2.0)
+        return launch_kernel(k_stats_partial<XF32, 2>, grid, dim3(kStatsThreads), 0, st, e0, nullptr, X, T, K, ldx,
+                             rows, part, p);
+    if (p == 1.0)
+        return launch_kernel(k_stats_partial<XF32, 1>, grid, dim3(kStatsThreads), 0, st, e0, nullptr, X, T, K, ldx,
+                             rows, part, p);
+    return launch_kernel(k_stats_partial<XF32, 0>, grid, dim3(kStatsThreads), 0, st, e0, nullptr, X, T, K, ldx,
+                         rows, part, p);
+}
+
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st, double* bsum, StageTimer tm) {
+                        int accumulate, double* part, hipStream_t st, double* bsum, StageTimer tm, double p) {
     int rows = 0;
     const int nchunks = stats_chunks(T, K, &rows);
     if (nchunks > 0) {
         dim3 grid((unsigned)((K + kStatsChans - 1) / kStatsChans), (unsigned)nchunks);
-        hipError_t e = xf32 ? launch_kernel(k_stats_partial<true>, grid, dim3(kStatsThreads), 0, st, tm.start,
-                                            nullptr, X, T, K, ldx, rows, part)
-                            : launch_kernel(k_stats_partial<false>, grid, dim3(kStatsThreads), 0, st, tm.start,
-                                            nullptr, X, T, K, ldx, rows, part);
+        hipError_t e = xf32 ? launch_partial<true>(grid, X, T, K, ldx, rows, part, p, st, tm.start)
+                            : launch_partial<false>(grid, X, T, K, ldx, rows, part, p, st, tm.start);
         if (e != hipSuccess) return e;
     }
     const dim3 g((unsigned)((K + kWave - 1) / kWave));
@@ -186,9 +203,9 @@ hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t 
 }
 
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
-                             float lambda_rel, float* s, hipStream_t st) {
+                             float lambda_rel, float p, float* s, hipStream_t st) {
     return launch_kernel(k_awq_scales, dim3(1), dim3(kScaleThreads), 0, st, nullptr, nullptr, ssq, n_tokens, K,
-                         (double)alpha, (double)lambda_rel, s);
+                         (double)alpha / (double)p, (double)lambda_rel, s);
 }
 
 }  // namespace ttq

@@ -182,7 +182,14 @@ size_t ttq_workspace_bytes(int64_t T, int64_t K, int64_t M, int bits, int group,
 
 ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, double* ssq,
                      int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    return ttq_stats_p(X, xt, T, K, ldx, 2.0f, ssq, accumulate, ws, ws_bytes, stream);
+}
+
+ttq_status ttq_stats_p(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, float p, double* msum,
+                       int accumulate, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
+    double* ssq = msum;
+    TTQ_REQUIRE(std::isfinite(p) && p > 0.f, "p must be finite and > 0");
     TTQ_REQUIRE(dim_ok(T), "T out of range");
     TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 8 == 0, "K must be a positive multiple of 8, at most 2^18");
     if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
@@ -191,7 +198,7 @@ ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, d
     if (ttq_status e = check_ws(ws, ws_bytes, need)) return e;
     if (T == 0 && accumulate) return TTQ_OK;
     return device_status(ttq::launch_stats(X, xt == TTQ_F32, T, K, ldx, ssq, accumulate,
-                                           (double*)ws, as_stream(stream)),
+                                           (double*)ws, as_stream(stream), nullptr, {}, (double)p),
                          "ttq_stats launch");
 }
 
@@ -205,8 +212,7 @@ ttq_status ttq_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float 
     TTQ_REQUIRE(std::isfinite(alpha) && alpha >= 0.f, "alpha must be finite and >= 0");
     TTQ_REQUIRE(std::isfinite(lambda_rel) && lambda_rel >= 0.f, "lambda_rel must be finite and >= 0");
     TTQ_REQUIRE(std::isfinite(p) && p > 0.f, "p must be finite and > 0");
-    if (p != 2.0f) return fail(TTQ_ERR_UNSUPPORTED, "only p = 2 (second-moment statistics) is implemented");
-    return device_status(ttq::launch_awq_scales(ssq, n_tokens, K, alpha, lambda_rel, s, as_stream(stream)),
+    return device_status(ttq::launch_awq_scales(ssq, n_tokens, K, alpha, lambda_rel, p, s, as_stream(stream)),
                          "ttq_awq_scales launch");
 }
 
@@ -279,7 +285,6 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     TTQ_REQUIRE(std::isfinite(a->alpha) && a->alpha >= 0.f, "alpha must be finite and >= 0");
     TTQ_REQUIRE(std::isfinite(a->lambda_rel) && a->lambda_rel >= 0.f, "lambda_rel must be finite and >= 0");
     TTQ_REQUIRE(std::isfinite(a->p) && a->p > 0.f, "p must be finite and > 0");
-    if (a->p != 2.0f) return fail(TTQ_ERR_UNSUPPORTED, "only p = 2 (second-moment statistics) is implemented");
     TTQ_REQUIRE(a->ssq == nullptr || aligned(a->ssq, 8), "ssq: not 8-byte aligned");
     TTQ_REQUIRE(a->s == nullptr || aligned(a->s, 16), "s: not 16-byte aligned");
     TTQ_REQUIRE(a->codes == nullptr || aligned(a->codes, 16), "codes: not 16-byte aligned");
@@ -316,15 +321,16 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                 return e;
         return TTQ_OK;
     };
-    // Statistics; the reduction also leaves the 64-channel block sums of c.
+    // Statistics (sums of |x|^p); the reduction also leaves the 64-channel
+    // block sums of c.
     double* bsum = (double*)(w + L.bsum);
-    if (ttq_status e = device_status(
-            ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch, st, bsum, timer(0)),
-            "stats"))
+    if (ttq_status e = device_status(ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch,
+                                                       st, bsum, timer(0), (double)a->p),
+                                     "stats"))
         return e;
     if (a->M == 0) {
         // No rows to quantize: the scales still form part of the prompt state.
-        if (ttq_status e = device_status(ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, s, st),
+        if (ttq_status e = device_status(ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, a->p, s, st),
                                          "scales"))
             return e;
         for (int i = 1; i < 4; ++i)
@@ -333,7 +339,7 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     }
     // The quantizer evaluates the scales of its channels from (ssq, lambda)
     // with the same arithmetic as ttq_awq_scales, and stores s.
-    const ttq::QScaleSrc qs{ssq, bsum, (double)a->lambda_rel, (double)a->T, (double)a->alpha / 2.0, s};
+    const ttq::QScaleSrc qs{ssq, bsum, (double)a->lambda_rel, (double)a->T, (double)a->alpha / (double)a->p, s};
     // Prompt-sized projections: the quantizer also writes the dequantized
     // weight (into the scratch area, free again once the statistics are
     // reduced) and the projection is a plain matrix-core GEMM on it.

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttq.so"
 TTQ_OK, TTQ_ERR_INVALID, TTQ_ERR_UNSUPPORTED, TTQ_ERR_DEVICE = 0, 1, 2, 3
 TTQ_F32, TTQ_BF16 = 0, 1
 
-EXPORTS = ("ttq_stats", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm",
+EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm",
            "ttq_lowrank_add", "ttq_workspace_bytes", "ttq_linear", "ttq_status_str",
            "ttq_last_error")
 
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "ttq_stats": [vp, i32, i64, i64, i64, vp, i32, vp, sz, vp],
+        "ttq_stats_p": [vp, i32, i64, i64, i64, f32, vp, i32, vp, sz, vp],
         "ttq_awq_scales": [vp, i64, i64, f32, f32, f32, vp, vp],
         "ttq_quantize_groups": [vp, i32, i64, i64, i64, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp],
         "ttq_qgemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, i32, i64, vp, sz, vp],
@@ -146,6 +147,17 @@ def ttq_stats(X: torch.Tensor, ssq: torch.Tensor, accumulate: bool = False,
     _check(lib().ttq_stats(_dev(X, "X"), _dtype_code(X), T, K, _ld(X, "X"), _dev(ssq, "ssq"),
                            int(bool(accumulate)), wp, wn, _stream(stream)))
     return ssq
+
+
+def ttq_stats_p(X: torch.Tensor, p: float, msum: torch.Tensor, accumulate: bool = False,
+                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if msum.dtype != torch.float64:
+        raise TypeError("msum must be float64")
+    T, K = X.shape
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_stats_p(_dev(X, "X"), _dtype_code(X), T, K, _ld(X, "X"), p, _dev(msum, "msum"),
+                             int(bool(accumulate)), wp, wn, _stream(stream)))
+    return msum
 
 
 def ttq_awq_scales(ssq: torch.Tensor, n_tokens: int, alpha: float, lambda_rel: float,

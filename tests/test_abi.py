@@ -82,6 +82,11 @@ def test_stats_rejects(L):
     assert st(FAKE, 1, 16, 128, 128, FAKE, 0, FAKE, 8, None) == 1         # workspace too small
     assert "workspace" in _err(L)
     assert st(FAKE, 1, 16, 128, 128, FAKE, 0, FAKE + 16, 1 << 30, None) == 1  # ws alignment
+    sp = L.ttq_stats_p
+    assert sp(FAKE, 1, 16, 128, 128, 0.0, FAKE, 0, FAKE, 1 << 30, None) == 1   # p <= 0
+    assert "p must be finite" in _err(L)
+    assert sp(FAKE, 1, 16, 128, 128, float("nan"), FAKE, 0, FAKE, 1 << 30, None) == 1
+    assert sp(FAKE, 1, 16, 100, 100, 1.0, FAKE, 0, FAKE, 1 << 30, None) == 1   # K % 8
 
 
 def test_scales_rejects(L):
@@ -90,8 +95,9 @@ def test_scales_rejects(L):
     assert sc(FAKE, 4, 128, -0.5, 0.01, 2.0, FAKE, None) == 1              # alpha < 0
     assert sc(FAKE, 4, 128, float("nan"), 0.01, 2.0, FAKE, None) == 1      # alpha NaN
     assert sc(FAKE, 4, 128, 0.5, float("inf"), 2.0, FAKE, None) == 1       # lambda
-    assert sc(FAKE, 4, 128, 0.5, 0.01, 1.0, FAKE, None) == 2               # p != 2
-    assert "p = 2" in _err(L)
+    assert sc(FAKE, 4, 128, 0.5, 0.01, 0.0, FAKE, None) == 1               # p <= 0
+    assert "p must be finite" in _err(L)
+    assert sc(FAKE, 4, 128, 0.5, 0.01, float("nan"), FAKE, None) == 1      # p NaN
     assert sc(FAKE, 4, 128, 0.5, 0.01, 2.0, FAKE + 4, None) == 1           # s alignment
 
 
@@ -142,9 +148,11 @@ def test_lowrank_and_linear_reject(L):
     assert L.ttq_lowrank_add(FAKE, 1, 8, 256, 256, None, FAKE, 64, 4, FAKE, 0, 64, FAKE, 1 << 20, None) == 1
     assert L.ttq_linear(None, FAKE, 1 << 20, None) == 1
     a = ttq.LinearArgs(X=FAKE, xt=1, T=8, K=256, ldx=256, W=FAKE, wt=1, M=64, ldw=256, alpha=0.5,
-                       lambda_rel=0.01, p=3.0, bits=4, group=32, B=None, A=None, rank=0, Y=FAKE, yt=0,
+                       lambda_rel=0.01, p=0.0, bits=4, group=32, B=None, A=None, rank=0, Y=FAKE, yt=0,
                        ldy=64)
-    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 2   # p != 2
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1   # p <= 0
+    a.p = float("inf")
+    assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1   # p not finite
     a.p = 2.0
     a.bits = 9
     assert L.ttq_linear(ctypes.byref(a), FAKE, 1 << 30, None) == 1

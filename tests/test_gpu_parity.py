@@ -97,10 +97,33 @@ def test_scales_zero_input_is_one(T):
     np.testing.assert_array_equal(host(s), np.ones(256, np.float32))
 
 
-def test_scales_unsupported_p(T):
-    with pytest.raises(T.TTQError) as e:
-        T.ttq_awq_scales(torch.ones(64, dtype=torch.float64, device="cuda"), 8, 0.5, 1e-2, p=1.0)
-    assert e.value.status == T.TTQ_ERR_UNSUPPORTED
+@pytest.mark.parametrize("p", [1.0, 3.0, 0.5])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_stats_and_scales_moment_p(T, p, xdt):
+    # [TTQ §method b4] p fixed in advance: sums of |x|^p and s = (c + lambda)^(alpha/p).
+    say(f"stats p={p} {xdt}")
+    key = "c1" if xdt == "f32" else "c2"
+    wl, d = _inputs(key, T=300, K=1096)
+    X = to_dev(d["X"], xdt)
+    ws = torch.empty(32 * 1096 * 8, dtype=torch.uint8, device="cuda")   # 32 fp64 partial rows
+    msum = T.ttq_stats_p(X, p, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
+    ref = oracle.stats(d["X"], xdt, p=p)
+    np.testing.assert_allclose(host(msum), ref, rtol=1e-12)
+    s = T.ttq_awq_scales(msum, 300, 0.5, 1e-2, p=p)
+    np.testing.assert_allclose(host(s), oracle.awq_scales(ref, 300, 0.5, 1e-2, p=p), rtol=1e-6)
+    # ttq_stats is the p = 2 case
+    ssq = T.ttq_stats(X, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
+    sq2 = T.ttq_stats_p(X, 2.0, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
+    np.testing.assert_array_equal(host(ssq), host(sq2))
+
+
+def test_stats_p_rejects_nonpositive(T):
+    X = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    m = torch.empty(64, dtype=torch.float64, device="cuda")
+    for p in (0.0, -2.0, float("nan")):
+        with pytest.raises(T.TTQError) as e:
+            T.ttq_stats_p(X, p, m, ws=torch.empty(32 * 64 * 8, dtype=torch.uint8, device="cuda"))
+        assert e.value.status == T.TTQ_ERR_INVALID
 
 
 # --------------------------------------------------------------- quantize
@@ -324,6 +347,32 @@ def test_linear_end_to_end(T, key, sizes):
     err = rel_fro(host(Y), ref["Y"])
     say(f"  Y rel err {err:.3e}")
     assert err < Y_TOL
+
+
+@pytest.mark.parametrize("p,key,sizes", [(1.0, "c2", dict(T=400, K=1024, M=300)),
+                                          (3.0, "c1", dict(T=64, K=768, M=200)),
+                                          (0.5, "c3", dict(T=256, K=2048, M=160))])
+def test_linear_moment_p(T, p, key, sizes):
+    # The whole layer with a moment order other than 2: statistics, the
+    # lambda and scales fused into the quantizer, codes and Y.
+    say(f"linear p={p} {key} {sizes}")
+    wl, d = _inputs(key, **sizes)
+    ref = oracle.linear(d["X"], wl.xdtype, d["W"], wl.wdtype, wl.bits, wl.group, wl.alpha,
+                        wl.lambda_rel, p=p)
+    st = T.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group)
+    Y = T.ttq_linear(to_dev(d["X"], wl.xdtype), to_dev(d["W"], wl.wdtype), wl.bits, wl.group, wl.alpha,
+                     wl.lambda_rel, p=p, state=st)
+    np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
+    s = host(st["s"])
+    np.testing.assert_allclose(s, ref["s"], rtol=S_TOL)
+    if np.array_equal(s, ref["s"]):
+        np.testing.assert_array_equal(host(st["scale_f16"]), ref["delta"])
+        np.testing.assert_array_equal(host(st["zero_f16"]), ref["zero"])
+        _check_codes(T, host(st["codes"]), ref["q"], ref["u"], wl.bits, wl.K)
+    assert rel_fro(host(Y), ref["Y"]) < (Y_TOL if wl.xdtype == "bf16" else 1e-4)
+    # the fused scales equal the standalone call's bit for bit
+    s2 = T.ttq_awq_scales(st["ssq"], wl.T, wl.alpha, wl.lambda_rel, p=p)
+    np.testing.assert_array_equal(host(s2), s)
 
 
 def test_linear_lowrank_unaligned_factor(T):
