@@ -51,7 +51,7 @@ import numpy as np
 __all__ = [
     "decode", "stats", "awq_scales", "quant_values", "group_rtn", "pack_codes",
     "unpack_codes", "dequant", "effective_weight", "project", "loss",
-    "lowrank_factors", "linear", "boundary_band",
+    "lowrank_factors", "lowrank_factors_randomized", "linear", "boundary_band",
 ]
 
 
@@ -288,6 +288,45 @@ def lowrank_factors(W: np.ndarray, wdtype: str, s: np.ndarray, rank: int):
     s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
     ws = decode(W, wdtype) * s64[None, :]
     U, S, Vt = np.linalg.svd(ws, full_matrices=False)
+    B = (U[:, :rank] * S[None, :rank]).astype(np.float32)
+    A = (Vt[:rank, :] / s64[None, :]).astype(np.float32)
+    return B, A
+
+
+def _orth(Y: np.ndarray) -> np.ndarray:
+    """Orthonormal basis of range(Y): the Q of Y = Q R with diag(R) > 0 (the
+    unique thin QR of a full-column-rank Y), via numpy's Householder QR."""
+    Q, R = np.linalg.qr(Y)
+    d = np.sign(np.diag(R))
+    d[d == 0] = 1.0
+    return Q * d[None, :]
+
+
+def lowrank_factors_randomized(W: np.ndarray, wdtype: str, s: np.ndarray, rank: int,
+                               omega: np.ndarray, q: int):
+    """Dynamic low-rank factors computed per prompt [TTQ §method b5: the
+    factors are dynamic].  Reading: the top-``rank`` factors of W diag(s)
+    estimated by randomized subspace iteration (Halko, Martinsson and Tropp,
+    "Finding structure with randomness", 2011: the range finder with q power
+    iterations, then the SVD of the small projected matrix).
+
+    ``omega`` is the l x K Gaussian test matrix (l >= rank), one test vector
+    per row, drawn by the caller.  With A_s = W diag(s):
+      Q = orth(A_s omega^T); q times: Q = orth(A_s orth(A_s^T Q));
+      C = Q^T A_s (l x K) = U~ S V^T;  U = Q U~;
+      B = U_r S_r, A = V_r^T diag(1/s), rounded to fp32 (as `lowrank_factors`).
+    fp64 throughout; orth is the Q of a thin QR with a positive diagonal.
+    """
+    s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
+    As = decode(W, wdtype) * s64[None, :]
+    Om = np.asarray(omega, dtype=np.float32).astype(np.float64)
+    Q = _orth(As @ Om.T)
+    for _ in range(q):
+        Z = _orth(As.T @ Q)
+        Q = _orth(As @ Z)
+    C = Q.T @ As
+    Ut, S, Vt = np.linalg.svd(C, full_matrices=False)
+    U = Q @ Ut
     B = (U[:, :rank] * S[None, :rank]).astype(np.float32)
     A = (Vt[:rank, :] / s64[None, :]).astype(np.float32)
     return B, A

@@ -460,3 +460,48 @@ def test_lowrank_residual_sign_and_scale():
     assert np.all(np.abs(w_eff - w) <= dl / (2 * s[None, :]) + slack)
     # and with the planted rank-16 part removed, the residual steps shrink
     assert np.median(out["delta"].astype(np.float64)) < np.median(out0["delta"].astype(np.float64))
+
+
+# Randomized subspace iteration for per-prompt factors ([TTQ §method b5]:
+# the factors are dynamic).
+
+def test_randomized_factors_full_sketch_is_exact_svd():
+    # With as many test vectors as W has columns the sketch spans everything,
+    # so the factors are the exact top-r SVD: Eckart-Young against the
+    # independent Jacobi eigenvalues of (W diag(s))^T (W diag(s)).
+    rng = np.random.default_rng(41)
+    W = synth.encode(rng.standard_normal((9, 8)), "f32")
+    s = (rng.random(8) + 0.5).astype(np.float32)
+    ws = W.astype(np.float64) * s.astype(np.float64)[None, :]
+    sig2 = _jacobi_eigenvalues((ws.T @ ws).tolist())
+    om = rng.standard_normal((8, 8)).astype(np.float32)
+    for q in (0, 2):
+        for r in (1, 3, 6):
+            B, A = oracle.lowrank_factors_randomized(W, "f32", s, r, om, q)
+            resid = (W.astype(np.float64) - B.astype(np.float64) @ A.astype(np.float64)) * s[None, :]
+            assert np.sum(resid ** 2) == pytest.approx(sum(sig2[r:]), rel=1e-5, abs=1e-9)
+
+
+def test_randomized_factors_converge_to_the_tail_energy():
+    # W diag(s) = U diag(sigma) V^T with a known spectrum (a gap after r):
+    # the residual energy falls towards the Eckart-Young tail sum_{i>=r}
+    # sigma_i^2 as power iterations are added.
+    rng = np.random.default_rng(42)
+    M, K, r, l = 70, 48, 5, 9
+    sig = np.concatenate([10.0 * 0.85 ** np.arange(r), 1.5 * 0.9 ** np.arange(K - r)])
+    U = np.linalg.qr(rng.standard_normal((M, K)))[0]
+    V = np.linalg.qr(rng.standard_normal((K, K)))[0]
+    s = (rng.random(K) + 0.5).astype(np.float32)
+    W = ((U * sig[None, :]) @ V.T / s.astype(np.float64)[None, :]).astype(np.float32)
+    ws = W.astype(np.float64) * s.astype(np.float64)[None, :]
+    tail = float(np.sum(sig[r:] ** 2))
+    om = rng.standard_normal((l, K)).astype(np.float32)
+    energies = []
+    for q in range(5):
+        B, A = oracle.lowrank_factors_randomized(W, "f32", s, r, om, q)
+        resid = ws - (B.astype(np.float64) @ A.astype(np.float64)) * s.astype(np.float64)[None, :]
+        energies.append(float(np.sum(resid ** 2)))
+    assert all(e >= tail * (1 - 1e-5) for e in energies)
+    assert energies[0] > tail * 1.01                     # one pass is visibly short of the optimum
+    assert energies[4] == pytest.approx(tail, rel=1e-4)  # four power iterations reach it
+    assert all(b <= a * (1 + 1e-6) for a, b in zip(energies, energies[1:]))
