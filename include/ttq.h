@@ -179,6 +179,35 @@ ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t 
                            void* stream);
 
 /*
+ * ttq_lowrank_factors — the dynamic low-rank factors of one prompt.
+ * [TTQ §method b5]: W = W_q + B A with factors formed per prompt.  The top
+ * `rank` factors of W diag(s) (s from this prompt's ttq_awq_scales) are
+ * estimated by randomized subspace iteration (Halko, Martinsson and Tropp,
+ * "Finding structure with randomness", 2011): with A_s = W diag(s),
+ *   Q = orth(A_s omega^T);  q times: Q = orth(A_s orth(A_s^T Q));
+ *   Q^T A_s = U~ S V^T;  B = Q U~_r S_r,  A = V_r^T diag(1/s),
+ * so that B A approximates W and B (A X) acts on the raw input; feed them
+ * to ttq_quantize_groups / ttq_linear with the same s.  orth() is CholQR2
+ * in fp64; the passes over W run on the matrix cores with fp32 accuracy;
+ * the small eigenproblem is a fp64 Jacobi iteration.
+ *   W: [M][K] bf16 (wt; fp32 W returns TTQ_ERR_UNSUPPORTED), stride ldw,
+ *   K a multiple of 32.  s: [K] fp32.  omega: [l][K] fp32, the caller's
+ *   Gaussian test vectors (one per row), 1 <= rank <= l <= 32, l <= M, K.
+ *   q: power iterations, 0..64.  Outputs B: [M][rank] fp32, A: [rank][K]
+ *   fp32, dense.  Singular vectors are determined up to sign (and within
+ *   repeated singular values); B A is the unique part.  A zero weight gives
+ *   zero factors.  ws: ttq_lowrank_factors_workspace_bytes(M, K, l) bytes,
+ *   256-byte aligned (it holds a bf16 transpose of W); results are bitwise
+ *   reproducible run to run.
+ */
+ttq_status ttq_lowrank_factors(const void* W, int wt, int64_t M, int64_t K, int64_t ldw,
+                               const float* s, const float* omega, int l, int q, int rank,
+                               float* B, float* A, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for ttq_lowrank_factors (0 for sizes it does not accept). */
+size_t ttq_lowrank_factors_workspace_bytes(int64_t M, int64_t K, int l);
+
+/*
  * Workspace size (bytes) sufficient for every call above and for ttq_linear
  * with these sizes (including the intermediate ssq, s, codes, steps and
  * zeros that ttq_linear keeps there when the caller does not supply them).

@@ -88,4 +88,14 @@ hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                           int64_t ldy, float* Zp, hipStream_t st, StageTimer tm = {});
 
+
+// Per-prompt low-rank factors (factors.hip): workspace regions and the call.
+struct FactorsLayout {
+    size_t wt, y, q1, qrow, op, gp, rinv, sig, u, bad, total;
+};
+FactorsLayout factors_layout(int64_t M, int64_t K, int l);
+bool factors_supported(bool wf32, int64_t M, int64_t K, int l, int rank);
+hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, const float* s, const float* om,
+                          int l, int q, int rank, float* B, float* A, char* ws, hipStream_t st);
+
 }  // namespace ttq

@@ -257,6 +257,33 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, c
                          "ttq_qgemm launch");
 }
 
+size_t ttq_lowrank_factors_workspace_bytes(int64_t M, int64_t K, int l) {
+    if (M <= 0 || K <= 0 || K > kMaxK || !dim_ok(M) || l < 1 || l > 32) return 0;
+    return ttq::factors_layout(M, K, l).total;
+}
+
+ttq_status ttq_lowrank_factors(const void* W, int wt, int64_t M, int64_t K, int64_t ldw, const float* s,
+                               const float* omega, int l, int q, int rank, float* B, float* A, void* ws,
+                               size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(dim_ok(M) && M > 0, "M must be positive");
+    TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 32 == 0, "K must be a positive multiple of 32, at most 2^18");
+    if (ttq_status e = check_matrix("W", W, wt, M, K, ldw)) return e;
+    TTQ_REQUIRE(l >= 1 && l <= 32, "l (test vectors) must be in [1, 32]");
+    TTQ_REQUIRE(rank >= 1 && rank <= l, "rank must be in [1, l]");
+    TTQ_REQUIRE(l <= M && l <= K, "l must not exceed M or K");
+    TTQ_REQUIRE(q >= 0 && q <= 64, "q (power iterations) must be in [0, 64]");
+    TTQ_REQUIRE(s != nullptr && aligned(s, 4), "s: null or misaligned");
+    TTQ_REQUIRE(omega != nullptr && aligned(omega, 4), "omega: null or misaligned");
+    TTQ_REQUIRE(B != nullptr && aligned(B, 4) && A != nullptr && aligned(A, 4), "B/A: null or misaligned");
+    if (wt == TTQ_F32) return fail(TTQ_ERR_UNSUPPORTED, "per-prompt factors need a bf16 weight");
+    TTQ_REQUIRE(ttq::factors_supported(false, M, K, l, rank), "sizes exceed the factor kernels' addressing");
+    if (ttq_status e = check_ws(ws, ws_bytes, ttq::factors_layout(M, K, l).total)) return e;
+    return device_status(ttq::launch_factors((const uint16_t*)W, M, K, ldw, s, omega, l, q, rank, B, A, (char*)ws,
+                                             as_stream(stream)),
+                         "ttq_lowrank_factors launch");
+}
+
 ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, const float* A,
                            const float* B, int64_t M, int rank, void* Y, int yt, int64_t ldy, void* ws,
                            size_t ws_bytes, void* stream) {

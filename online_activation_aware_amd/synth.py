@@ -158,6 +158,13 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
     return out
 
 
+def test_vectors(l: int, K: int, seed: int = 0) -> np.ndarray:
+    """l Gaussian test vectors of length K (rows), fp32: the random input of
+    the randomized low-rank factorization, drawn by the caller."""
+    rng = np.random.default_rng(np.random.SeedSequence(7000 + seed))
+    return rng.standard_normal((l, K)).astype(np.float32)
+
+
 def as_float(a: np.ndarray, dtype: str) -> np.ndarray:
     """Encoded array -> exact fp32 values (bf16 widened)."""
     return bf16_bits_to_f32(a) if dtype == "bf16" else np.asarray(a, dtype=np.float32)

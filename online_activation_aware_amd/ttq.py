@@ -19,8 +19,8 @@ TTQ_OK, TTQ_ERR_INVALID, TTQ_ERR_UNSUPPORTED, TTQ_ERR_DEVICE = 0, 1, 2, 3
 TTQ_F32, TTQ_BF16 = 0, 1
 
 EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm",
-           "ttq_lowrank_add", "ttq_workspace_bytes", "ttq_linear", "ttq_status_str",
-           "ttq_last_error")
+           "ttq_lowrank_add", "ttq_lowrank_factors", "ttq_lowrank_factors_workspace_bytes",
+           "ttq_workspace_bytes", "ttq_linear", "ttq_status_str", "ttq_last_error")
 
 
 class TTQError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "ttq_qgemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, i32, i64, vp, sz, vp],
         "ttq_lowrank_add": [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, i32, i64, vp, sz, vp],
         "ttq_workspace_bytes": [i64, i64, i64, i32, i32, i32],
+        "ttq_lowrank_factors": [vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
+        "ttq_lowrank_factors_workspace_bytes": [i64, i64, i32],
         "ttq_linear": [ctypes.POINTER(LinearArgs), vp, sz, vp],
         "ttq_status_str": [i32],
         "ttq_last_error": [],
@@ -74,6 +76,7 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = argtypes
         fn.restype = ctypes.c_int
     L.ttq_workspace_bytes.restype = ctypes.c_size_t
+    L.ttq_lowrank_factors_workspace_bytes.restype = ctypes.c_size_t
     L.ttq_status_str.restype = ctypes.c_char_p
     L.ttq_last_error.restype = ctypes.c_char_p
     _lib_handle = L
@@ -213,6 +216,29 @@ def ttq_lowrank_add(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, Y: torch.
                                  _dev(B, "B"), M, rank, _dev(Y, "Y"), _dtype_code(Y), _ld(Y, "Y"),
                                  wp, wn, _stream(stream)))
     return Y
+
+
+def ttq_lowrank_factors(W: torch.Tensor, s: torch.Tensor, omega: torch.Tensor, rank: int, q: int,
+                        B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, stream=None):
+    """Per-prompt factors of W diag(s): returns (B [M][rank], A [rank][K])."""
+    M, K = W.shape
+    l = omega.shape[0]
+    if omega.shape != (l, K) or omega.dtype != torch.float32:
+        raise ValueError("omega must be float32 [l][K]")
+    if B is None:
+        B = torch.empty((M, rank), dtype=torch.float32, device=W.device)
+    if A is None:
+        A = torch.empty((rank, K), dtype=torch.float32, device=W.device)
+    if ws is None:
+        n = lib().ttq_lowrank_factors_workspace_bytes(M, K, l)
+        if n == 0:
+            raise ValueError("no factorization accepts these sizes")
+        ws = torch.empty(n, dtype=torch.uint8, device=W.device)
+    _check(lib().ttq_lowrank_factors(_dev(W, "W"), _dtype_code(W), M, K, _ld(W, "W"), _dev(s, "s"),
+                                     _dev(omega, "omega"), l, q, rank, _dev(B, "B"), _dev(A, "A"),
+                                     ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return B, A
 
 
 def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: float,

@@ -165,3 +165,25 @@ def test_lowrank_and_linear_reject(L):
     a.stage_events = None
     a.T = 0
     assert L.ttq_linear(ctypes.byref(a), None, 0, None) == 0          # empty prompt
+
+
+def test_lowrank_factors_rejects(L):
+    f = L.ttq_lowrank_factors
+    ok = dict(W=FAKE, wt=1, M=256, K=512, ldw=512, s=FAKE, om=FAKE, l=24, q=2, rank=16, B=FAKE, A=FAKE,
+              ws=FAKE, wn=1 << 30, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["W"], a["wt"], a["M"], a["K"], a["ldw"], a["s"], a["om"], a["l"], a["q"], a["rank"],
+                 a["B"], a["A"], a["ws"], a["wn"], a["st"])
+    assert call(K=500, ldw=500) == 1                    # K % 32
+    assert call(l=33) == 1 and call(l=0) == 1
+    assert call(rank=25) == 1 and call(rank=0) == 1     # rank <= l
+    assert call(M=16) == 1                              # l <= M
+    assert call(q=-1) == 1
+    assert call(s=None) == 1 and call(om=None) == 1 and call(B=None) == 1
+    assert call(wt=0) == 2                              # fp32 weight: not implemented
+    assert call(wn=64) == 1                             # workspace too small
+    assert "workspace" in _err(L)
+    assert L.ttq_lowrank_factors_workspace_bytes(256, 512, 24) > 256 * 512 * 2
+    assert L.ttq_lowrank_factors_workspace_bytes(256, 512, 40) == 0
