@@ -75,22 +75,42 @@ def algorithmic_bytes(wl) -> dict:
     }
 
 
-def harness_lowrank_factors(W64, s, rank, seed=0):
-    """Input preparation for low-rank workloads (not timed): top-`rank`
-    factors of W diag(s) by randomized subspace iteration, B = U S,
-    A = V^T diag(1/s), in fp32."""
-    import numpy as np
-    rng = np.random.default_rng(seed)
-    s64 = s.astype(np.float64)
-    Ws = W64 * s64[None, :]
-    Q = np.linalg.qr(Ws @ rng.standard_normal((Ws.shape[1], rank + 8)))[0]
-    for _ in range(4):
-        Q = np.linalg.qr(Ws @ (Ws.T @ Q))[0]
-    U, S, Vt = np.linalg.svd(Q.T @ Ws, full_matrices=False)
-    U = Q @ U
-    B = (U[:, :rank] * S[None, :rank]).astype(np.float32)
-    A = (Vt[:rank] / s64[None, :]).astype(np.float32)
-    return B, A
+def time_factors(ttq, Ws, s, om, wl, l, q, args) -> dict:
+    """ttq_lowrank_factors over the rotating weight copies, one call per copy
+    captured in a HIP graph (its small kernels are launch-bound eagerly)."""
+    import torch
+    n = len(Ws)
+    Bf = torch.empty((wl.M, wl.rank), dtype=torch.float32, device=s.device)
+    Af = torch.empty((wl.rank, wl.K), dtype=torch.float32, device=s.device)
+    wsf = torch.empty(ttq.lib().ttq_lowrank_factors_workspace_bytes(wl.M, wl.K, l), dtype=torch.uint8,
+                      device=s.device)
+
+    def calls():
+        for W in Ws:
+            ttq.ttq_lowrank_factors(W, s, om, wl.rank, q, B=Bf, A=Af, ws=wsf)
+    calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / n))
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * n) * 1e3
+    passes = 2 * q + 2
+    wbytes = wl.M * wl.K * 2
+    return {"us": round(us, 2), "l": l, "q": q, "passes_over_w": passes,
+            "method": "randomized subspace iteration (CholQR2, Jacobi), bf16 transpose of W once",
+            "w_stream_gbs": round((passes + 2) * wbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(wl, data, B=None, A=None) -> dict:
@@ -178,14 +198,21 @@ def main(argv=None) -> int:
 
     B = A = None
     B_h = A_h = None
+    factors = None
     if wl.rank:
+        # Per-prompt factors of W diag(s) on the GPU (randomized subspace
+        # iteration, l = rank + 8 test vectors, q = 2 power iterations); the
+        # layer below uses them, and they are timed on their own.
         ssq = torch.empty(wl.K, dtype=torch.float64, device=dev)
         ttq.ttq_stats(X0, ssq, ws=ttq.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, wl.rank, device=dev))
-        s0 = ttq.ttq_awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel).cpu().numpy()
-        w64 = synth.as_float(data["W"], wl.wdtype).astype(np.float64)
-        B_h, A_h = harness_lowrank_factors(w64, s0, wl.rank)
-        B, A = torch.from_numpy(B_h).to(dev), torch.from_numpy(A_h).to(dev)
-        log("low-rank factors prepared (harness, untimed)")
+        s0 = ttq.ttq_awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel)
+        l_f, q_f = wl.rank + 8, 2
+        om = torch.from_numpy(synth.test_vectors(l_f, wl.K, seed=0)).to(dev)
+        B, A = ttq.ttq_lowrank_factors(W0, s0, om, wl.rank, q_f)
+        torch.cuda.synchronize()
+        B_h, A_h = B.cpu().numpy(), A.cpu().numpy()
+        factors = time_factors(ttq, Ws, s0, om, wl, l_f, q_f, args)
+        log(f"  factors   {factors['us']:8.2f} us  (l={l_f}, q={q_f}, {factors['passes_over_w']} passes over W)")
 
     st = ttq.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group, device=dev)
     ws = ttq.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, wl.rank, device=dev)
@@ -334,6 +361,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "stages": breakdown,
         "decode": decode,
+        "factors": factors,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -23,6 +23,7 @@ namespace ttq {
 
 constexpr int kFMaxL = 32;
 constexpr int kGramRows = 64;                     // rows per Gram partial
+constexpr int kGramStage = 64;                    // rows staged in LDS at a time
 
 // Wt[j][o] = W[o][j] for o < M, 0 for M <= o < ldt (64 x 64 tiles via LDS).
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ W, int64_t M, int64_t K,
@@ -50,50 +51,76 @@ __global__ __launch_bounds__(256) void k_scale_cols(const float* __restrict__ in
 }
 
 // Gram partials: chunk c (rows 64 c .. 64 c + 63 of Y [N][l], each row scaled
-// by rs[n] if given) -> Gp[c][a][b] = sum_n y_na y_nb in fp64, rows in order.
+// by rs[n] if given) -> Gp[c][a][b] = sum_n y_na y_nb in fp64, rows in order
+// (staged through LDS).
 __global__ __launch_bounds__(1024) void k_gram_partial(const float* __restrict__ Y, int64_t N, int l,
                                                        const float* __restrict__ rs, double* __restrict__ Gp) {
-    __shared__ double ys[kGramRows][kFMaxL];
-    const int64_t n0 = (int64_t)blockIdx.x * kGramRows;
-    for (int idx = threadIdx.x; idx < kGramRows * l; idx += 1024) {
-        const int r = idx / l, c = idx % l;
-        const int64_t n = n0 + r;
-        double v = 0.0;
-        if (n < N) v = (double)Y[n * l + c] * (rs ? (double)rs[n] : 1.0);
-        ys[r][c] = v;
-    }
-    __syncthreads();
+    __shared__ double ys[kGramStage][kFMaxL];
     const int a = threadIdx.x / kFMaxL, b = threadIdx.x % kFMaxL;
-    if (a < l && b < l) {
-        double acc = 0.0;
-        for (int r = 0; r < kGramRows; ++r) acc = __builtin_fma(ys[r][a], ys[r][b], acc);
-        Gp[((int64_t)blockIdx.x * l + a) * l + b] = acc;
+    double acc = 0.0;
+    for (int st = 0; st < kGramRows; st += kGramStage) {
+        const int64_t n0 = (int64_t)blockIdx.x * kGramRows + st;
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < kGramStage * l; idx += 1024) {
+            const int r = idx / l, c = idx % l;
+            const int64_t n = n0 + r;
+            double v = 0.0;
+            if (n < N) v = (double)Y[n * l + c] * (rs ? (double)rs[n] : 1.0);
+            ys[r][c] = v;
+        }
+        __syncthreads();
+        if (a < l && b < l)
+            for (int r = 0; r < kGramStage; ++r) acc = __builtin_fma(ys[r][a], ys[r][b], acc);
     }
+    if (a < l && b < l) Gp[((int64_t)blockIdx.x * l + a) * l + b] = acc;
 }
 
-// One workgroup: G = sum of the partials in chunk order; G = R^T R (R upper,
-// right-looking Cholesky); Rinv = R^-1 (upper).  `bad` records whether a
-// pivot was <= 0 (diagnostics only).
-__global__ __launch_bounds__(1024) void k_chol_inv(const double* __restrict__ Gp, int nchunks, int l,
-                                                   double* __restrict__ Rinv, int* __restrict__ bad) {
+// Sum of the chunk partials Gp[c] (l x l) by a 1024-thread block, into
+// out[a][b] (LDS, row stride kFMaxL + 1): four groups of 256 threads add the
+// chunks c = g, g + 4, ... (all loads independent), then the four group sums
+// are added in group order.  Fixed order: bitwise reproducible.
+__device__ void sum_partials(const double* __restrict__ Gp, int nchunks, int l, double (*part)[kFMaxL * kFMaxL],
+                             double (*out)[kFMaxL + 1]) {
+    const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
+    const int ne = l * l;
+    for (int e = t; e < ne; e += 256) {
+        double acc = 0.0;
+#pragma unroll 8
+        for (int c = grp; c < nchunks; c += 4) acc += Gp[(int64_t)c * ne + e];
+        part[grp][e] = acc;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < ne; e += 1024)
+        out[e / l][e % l] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+    __syncthreads();
+}
+
+// G[a][b] = sum of the chunk partials.
+__global__ __launch_bounds__(1024) void k_gram_reduce(const double* __restrict__ Gp, int nchunks, int l,
+                                                      double* __restrict__ G) {
+    __shared__ double part[4][kFMaxL * kFMaxL];
     __shared__ double g[kFMaxL][kFMaxL + 1];
-    __shared__ double rinv[kFMaxL][kFMaxL + 1];
+    sum_partials(Gp, nchunks, l, part, g);
+    for (int e = threadIdx.x; e < l * l; e += 1024) G[e] = g[e / l][e % l];
+}
+
+// One workgroup: G = sum of the partials (sum_partials); G = R^T R (R upper,
+// right-looking Cholesky, one thread per entry), written to Rout.  A pivot
+// <= 0 (exactly dependent columns, e.g. a zero weight) gives R_kk = 1 and
+// R_kj = 0, so that column of Y R^-1 is the (zero) residual; `bad` counts
+// such pivots (diagnostics only).
+__global__ __launch_bounds__(1024) void k_chol(const double* __restrict__ Gp, int nchunks, int l,
+                                               double* __restrict__ Rout, int* __restrict__ bad) {
+    __shared__ double part[4][kFMaxL * kFMaxL];
+    __shared__ double g[kFMaxL][kFMaxL + 1];
     __shared__ int nbad;
     const int a = threadIdx.x / kFMaxL, b = threadIdx.x % kFMaxL;
     if (threadIdx.x == 0) nbad = 0;
     const bool in = a < l && b < l;
-    if (in) {
-        double acc = 0.0;
-        for (int c = 0; c < nchunks; ++c) acc += Gp[((int64_t)c * l + a) * l + b];
-        g[a][b] = acc;
-    }
-    __syncthreads();
+    sum_partials(Gp, nchunks, l, part, g);
     for (int k = 0; k < l; ++k) {
-        // Row k of R: R_kk = sqrt(g_kk), R_kj = g_kj / R_kk (kept in g's row k).
         const double d = g[k][k];
         __syncthreads();
-        // A pivot <= 0 (exactly dependent columns, e.g. a zero weight): R_kk = 1
-        // and R_kj = 0, so that column of Y R^-1 is the (zero) residual.
         if (a == k && in && b >= k)
             g[k][b] = d > 0.0 ? ((b == k) ? __builtin_sqrt(d) : g[k][b] / __builtin_sqrt(d)) : (b == k ? 1.0 : 0.0);
         if (threadIdx.x == 0 && !(d > 0.0)) nbad += 1;
@@ -101,180 +128,157 @@ __global__ __launch_bounds__(1024) void k_chol_inv(const double* __restrict__ Gp
         if (in && a > k && b >= a) g[a][b] -= g[k][a] * g[k][b];
         __syncthreads();
     }
-    // Rinv column b by back substitution (one thread per column).
-    if (threadIdx.x < l) {
-        const int c = threadIdx.x;
-        for (int i = l - 1; i >= 0; --i) {
-            double v = (i == c) ? 1.0 : 0.0;
-            for (int k = i + 1; k <= c; ++k) v -= g[i][k] * rinv[k][c];
-            rinv[i][c] = (i <= c) ? v / g[i][i] : 0.0;
-        }
-    }
-    __syncthreads();
-    if (in) Rinv[a * l + b] = rinv[a][b];
+    if (in) Rout[a * l + b] = b >= a ? g[a][b] : 0.0;
     if (threadIdx.x == 0) *bad = nbad;
 }
 
-// out = (rs o Y) Rinv, per row n of Y [N][l], in fp64, rounded to fp32.
+// out = (rs o Y) R^-1 per row n of Y [N][l]: q R = y by forward substitution
+// (q_c = (y_c - sum_{k<c} q_k R_kc) / R_cc), in fp64, rounded to fp32.  A
+// group of 32 lanes owns one row (lane c computes q_c; the q_k it needs come
+// from lanes k < c by shuffles, in order).
 // mode 0: out [N][l].  mode 1: out [l][ldo] transposed, times cs[n] if given
 // (columns N <= n < ldo are zero).
-__global__ __launch_bounds__(256) void k_apply_rinv(const float* __restrict__ Y, int64_t N, int l,
-                                                    const float* __restrict__ rs, const double* __restrict__ Rinv,
-                                                    int mode, const float* __restrict__ cs, float* __restrict__ out,
-                                                    int64_t ldo) {
-    __shared__ double ri[kFMaxL * kFMaxL];
-    for (int i = threadIdx.x; i < l * l; i += 256) ri[i] = Rinv[i];
+__global__ __launch_bounds__(256) void k_apply_r(const float* __restrict__ Y, int64_t N, int l,
+                                                 const float* __restrict__ rs, const double* __restrict__ R,
+                                                 int mode, const float* __restrict__ cs, float* __restrict__ out,
+                                                 int64_t ldo) {
+    __shared__ double rr[kFMaxL * kFMaxL];
+    for (int i = threadIdx.x; i < l * l; i += 256) rr[i] = R[i];
     __syncthreads();
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int c = threadIdx.x & 31;
+    const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 32;
     const int64_t lim = mode == 0 ? N : ldo;
-    if (n >= lim) return;
+    if (n >= lim) return;                         // uniform over the 32 lanes of a row
     if (n >= N) {                                 // padding columns of the transposed operand
-        for (int c = 0; c < l; ++c) out[c * ldo + n] = 0.f;
+        if (c < l) out[c * ldo + n] = 0.f;
         return;
     }
-    // Static indices throughout (y stays in registers); l <= 32 is uniform.
-    double y[kFMaxL];
-    const double sc = rs ? (double)rs[n] : 1.0;
-#pragma unroll
-    for (int k = 0; k < kFMaxL; ++k) y[k] = k < l ? (double)Y[n * l + k] * sc : 0.0;
-    const double cm = (mode == 1 && cs) ? (double)cs[n] : 1.0;
-#pragma unroll
-    for (int c = 0; c < kFMaxL; ++c) {
-        if (c < l) {
-            double v = 0.0;
-#pragma unroll
-            for (int k = 0; k <= c; ++k) v = __builtin_fma(y[k], ri[k * l + c], v);
-            if (mode == 0) out[n * l + c] = (float)v;
-            else out[c * ldo + n] = (float)(v * cm);
-        }
+    const double y = c < l ? (double)Y[n * l + c] * (rs ? (double)rs[n] : 1.0) : 0.0;
+    double v = y, q = 0.0;
+    for (int k = 0; k < l; ++k) {
+        // q_k is final once lane k has subtracted the terms of lanes < k.
+        const double qk = __shfl(c == k ? v / rr[k * l + k] : 0.0, k, 32);
+        if (c == k) q = qk;
+        if (c > k) v = __builtin_fma(-qk, rr[k * l + c], v);
+    }
+    if (c < l) {
+        if (mode == 0) out[n * l + c] = (float)q;
+        else out[c * ldo + n] = (float)(q * ((cs != nullptr) ? (double)cs[n] : 1.0));
     }
 }
 
-// Symmetric l x l eigenproblem (G = sum of Gram partials) by cyclic Jacobi
-// on one wave: a sweep is l-1 rounds of l/2 disjoint rotations (round-robin
-// pairing), each applied to the columns, then to the rows, and accumulated
-// into V.  Output: eigenvalues descending as sigma = sqrt(max(ev, 0)) and
-// the matching eigenvectors as columns of U [l][l].
-__global__ __launch_bounds__(64) void k_jacobi(const double* __restrict__ Gp, int nchunks, int l,
-                                               double* __restrict__ sig, double* __restrict__ U) {
+// Symmetric l x l eigenproblem G [l][l] by cyclic Jacobi.  A sweep is l-1
+// rounds of l/2 disjoint rotations (round-robin pairing); in a round every
+// index i has a partner p_i and a pair (c_i, s_i) with column i of the
+// rotation J equal to c_i e_i + s_i e_{p_i}, so one thread per entry forms
+// (J^T G J)[i][j] and (V J)[i][j] from the previous round's values.
+// Output: eigenvalues descending as sigma = sqrt(max(ev, 0)) and the matching
+// eigenvectors as columns of U [l][l].
+__global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, int l, double* __restrict__ sig,
+                                                 double* __restrict__ U) {
     __shared__ double a[kFMaxL][kFMaxL + 1];
     __shared__ double v[kFMaxL][kFMaxL + 1];
-    __shared__ double cs_[kFMaxL / 2], sn_[kFMaxL / 2];
-    __shared__ int pp[kFMaxL / 2], qq[kFMaxL / 2];
+    __shared__ double rc[kFMaxL], rs_[kFMaxL];
+    __shared__ int ptn[kFMaxL];
+    __shared__ double wsum[16];
     __shared__ int order[kFMaxL];
-    __shared__ double offs;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int i = tid / l, j = tid % l;           // blockDim = l*l rounded up to whole waves
+    const bool in = tid < l * l;
     const int n = l + (l & 1);                    // even count for the pairing (a dummy index if odd)
-    for (int idx = lane; idx < kFMaxL * kFMaxL; idx += 64) {
-        const int i = idx / kFMaxL, j = idx % kFMaxL;
-        double acc = 0.0;
-        if (i < l && j < l)
-            for (int c = 0; c < nchunks; ++c) acc += Gp[((int64_t)c * l + i) * l + j];
-        a[i][j] = acc;
+    if (in) {
+        a[i][j] = G[i * l + j];
         v[i][j] = (i == j) ? 1.0 : 0.0;
     }
     __syncthreads();
     double scale = 0.0;
-    for (int i = 0; i < l; ++i) scale += a[i][i];
+    for (int k = 0; k < l; ++k) scale += a[k][k];
     for (int sweep = 0; sweep < 30; ++sweep) {
-        if (lane == 0) {
-            double o = 0.0;
-            for (int i = 0; i < l; ++i)
-                for (int j = 0; j < l; ++j)
-                    if (i != j) o += a[i][j] * a[i][j];
-            offs = o;
-        }
+        // Off-diagonal mass, reduced over the block in a fixed order.
+        double o = (in && i != j) ? a[i][j] * a[i][j] : 0.0;
+        for (int m = 32; m >= 1; m >>= 1) o += __shfl_xor(o, m);
+        if ((tid & 63) == 0) wsum[tid >> 6] = o;
         __syncthreads();
-        if (!(offs > 1e-30 * scale * scale)) break;
+        double tot = 0.0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += wsum[w];
+        // Stop when the off-diagonal mass is at the rounding level of the
+        // largest eigenvalues (cyclic Jacobi converges quadratically).
+        if (!(tot > 1e-28 * scale * scale)) break;
         for (int round = 0; round < n - 1; ++round) {
-            // Round-robin pairs: index n-1 fixed, the others rotate.
-            if (lane < n / 2) {
+            if (tid < n / 2) {
                 int p, q;
-                if (lane == 0) { p = n - 1; q = round % (n - 1); }
-                else { p = (round + lane) % (n - 1); q = (round + n - 1 - lane) % (n - 1); }
+                if (tid == 0) { p = n - 1; q = round % (n - 1); }
+                else { p = (round + tid) % (n - 1); q = (round + n - 1 - tid) % (n - 1); }
                 if (p > q) { const int t = p; p = q; q = t; }
-                double c = 1.0, s = 0.0;
-                if (q < l && p < l && a[p][q] != 0.0) {
+                double c = 1.0, sn = 0.0;
+                if (q < l && a[p][q] != 0.0) {
                     const double th = (a[q][q] - a[p][p]) / (2.0 * a[p][q]);
                     const double t = (th >= 0.0 ? 1.0 : -1.0) / (__builtin_fabs(th) + __builtin_sqrt(th * th + 1.0));
                     c = 1.0 / __builtin_sqrt(t * t + 1.0);
-                    s = t * c;
+                    sn = t * c;
                 }
-                pp[lane] = p; qq[lane] = q; cs_[lane] = c; sn_[lane] = s;
+                // J[p][p] = c, J[q][p] = -s, J[p][q] = s, J[q][q] = c.
+                if (p < l) { ptn[p] = q < l ? q : p; rc[p] = c; rs_[p] = q < l ? -sn : 0.0; }
+                if (q < l) { ptn[q] = p; rc[q] = c; rs_[q] = sn; }
             }
             __syncthreads();
-            // Columns: a[:, p], a[:, q] and v[:, p], v[:, q].
-            for (int idx = lane; idx < (n / 2) * l; idx += 64) {
-                const int r = idx / l, k = idx % l;
-                const int p = pp[r], q = qq[r];
-                if (q >= l) continue;
-                const double c = cs_[r], s = sn_[r];
-                const double akp = a[k][p], akq = a[k][q];
-                a[k][p] = c * akp - s * akq;
-                a[k][q] = s * akp + c * akq;
-                const double vkp = v[k][p], vkq = v[k][q];
-                v[k][p] = c * vkp - s * vkq;
-                v[k][q] = s * vkp + c * vkq;
+            double na = 0.0, nv = 0.0;
+            if (in) {
+                const int pi = ptn[i], pj = ptn[j];
+                const double ci = rc[i], si = rs_[i], cj = rc[j], sj = rs_[j];
+                na = ci * (cj * a[i][j] + sj * a[i][pj]) + si * (cj * a[pi][j] + sj * a[pi][pj]);
+                nv = cj * v[i][j] + sj * v[i][pj];
             }
             __syncthreads();
-            // Rows: a[p, :], a[q, :].
-            for (int idx = lane; idx < (n / 2) * l; idx += 64) {
-                const int r = idx / l, k = idx % l;
-                const int p = pp[r], q = qq[r];
-                if (q >= l) continue;
-                const double c = cs_[r], s = sn_[r];
-                const double apk = a[p][k], aqk = a[q][k];
-                a[p][k] = c * apk - s * aqk;
-                a[q][k] = s * apk + c * aqk;
-            }
+            if (in) { a[i][j] = na; v[i][j] = nv; }
             __syncthreads();
         }
     }
     // Sort by eigenvalue, descending (ties keep index order).
-    if (lane == 0) {
-        for (int i = 0; i < l; ++i) order[i] = i;
-        for (int i = 0; i < l; ++i) {
-            int best = i;
-            for (int j = i + 1; j < l; ++j)
-                if (a[order[j]][order[j]] > a[order[best]][order[best]]) best = j;
-            const int t = order[i]; order[i] = order[best]; order[best] = t;
+    if (tid == 0) {
+        for (int k = 0; k < l; ++k) order[k] = k;
+        for (int k = 0; k < l; ++k) {
+            int best = k;
+            for (int m = k + 1; m < l; ++m)
+                if (a[order[m]][order[m]] > a[order[best]][order[best]]) best = m;
+            const int t = order[k]; order[k] = order[best]; order[best] = t;
         }
     }
     __syncthreads();
-    if (lane < l) {
-        const double ev = a[order[lane]][order[lane]];
-        sig[lane] = __builtin_sqrt(ev > 0.0 ? ev : 0.0);
+    if (tid < l) {
+        const double ev = a[order[tid]][order[tid]];
+        sig[tid] = __builtin_sqrt(ev > 0.0 ? ev : 0.0);
     }
-    for (int idx = lane; idx < l * l; idx += 64) {
-        const int i = idx / l, k = idx % l;
-        U[i * l + k] = v[i][order[k]];
-    }
+    if (in) U[i * l + j] = v[i][order[j]];
 }
 
-// B[o][k] = sig_k * sum_i Q[o][i] U[i][k]   (k < rank).
+static unsigned jacobi_threads(int l) { return (unsigned)((l * l + 63) / 64 * 64); }
+
+// B[o][k] = sig_k * sum_i Q[o][i] U[i][k]   (k < rank), one thread per entry.
 __global__ __launch_bounds__(256) void k_form_b(const float* __restrict__ Q, int64_t M, int l, int rank,
                                                 const double* __restrict__ U, const double* __restrict__ sig,
                                                 float* __restrict__ B) {
-    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (o >= M) return;
-    for (int k = 0; k < rank; ++k) {
-        double acc = 0.0;
-        for (int i = 0; i < l; ++i) acc = __builtin_fma((double)Q[o * l + i], U[i * l + k], acc);
-        B[o * rank + k] = (float)(acc * sig[k]);
-    }
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * rank) return;
+    const int64_t o = idx / rank;
+    const int k = (int)(idx % rank);
+    double acc = 0.0;
+    for (int i = 0; i < l; ++i) acc = __builtin_fma((double)Q[o * l + i], U[i * l + k], acc);
+    B[idx] = (float)(acc * sig[k]);
 }
 
-// A[k][j] = (sum_i P[j][i] U[i][k]) / sig_k   (k < rank; P = W^T Q).
+// A[k][j] = (sum_i P[j][i] U[i][k]) / sig_k   (k < rank; P = W^T Q), one
+// thread per entry (consecutive threads: consecutive j).
 __global__ __launch_bounds__(256) void k_form_a(const float* __restrict__ P, int64_t K, int l, int rank,
                                                 const double* __restrict__ U, const double* __restrict__ sig,
                                                 float* __restrict__ A) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= K) return;
-    for (int k = 0; k < rank; ++k) {
-        double acc = 0.0;
-        for (int i = 0; i < l; ++i) acc = __builtin_fma((double)P[j * l + i], U[i * l + k], acc);
-        A[k * K + j] = sig[k] > 0.0 ? (float)(acc / sig[k]) : 0.0f;
-    }
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= K * rank) return;
+    const int k = (int)(idx / K);
+    const int64_t j = idx % K;
+    double acc = 0.0;
+    for (int i = 0; i < l; ++i) acc = __builtin_fma((double)P[j * l + i], U[i * l + k], acc);
+    A[idx] = sig[k] > 0.0 ? (float)(acc / sig[k]) : 0.0f;
 }
 
 // ------------------------------------------------------------------ host
@@ -295,6 +299,7 @@ FactorsLayout factors_layout(int64_t M, int64_t K, int l) {
     F.op = off;    off += up((size_t)l * NP * 4);         // next pass operand [l][K or M32]
     F.gp = off;    off += up((size_t)((N + kGramRows - 1) / kGramRows) * l * l * 8);
     F.rinv = off;  off += up((size_t)l * l * 8);
+    F.g = off;     off += up((size_t)l * l * 8);
     F.sig = off;   off += up((size_t)l * 8);
     F.u = off;     off += up((size_t)l * l * 8);
     F.bad = off;   off += up(sizeof(int) * 2);
@@ -317,7 +322,8 @@ hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, 
     float* Qrow = (float*)(ws + F.qrow);
     float* op = (float*)(ws + F.op);
     double* Gp = (double*)(ws + F.gp);
-    double* Rinv = (double*)(ws + F.rinv);
+    double* Rm = (double*)(ws + F.rinv);
+    double* Gm = (double*)(ws + F.g);
     double* sig = (double*)(ws + F.sig);
     double* U = (double*)(ws + F.u);
     int* bad = (int*)(ws + F.bad);
@@ -330,28 +336,29 @@ hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, 
     auto cholqr2 = [&](const float* Yin, int64_t N, const float* rs, const float* cs, int64_t ldo,
                        float* qrow) -> hipError_t {
         const unsigned nch = (unsigned)((N + kGramRows - 1) / kGramRows);
+        auto rows_grid = [](int64_t n) { return dim3((unsigned)((n * 32 + 255) / 256)); };
         hipError_t r;
         if ((r = launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, Yin, N, l, rs, Gp)))
             return r;
-        if ((r = launch_kernel(k_chol_inv, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp,
-                               (int)nch, l, Rinv, bad)))
+        if ((r = launch_kernel(k_chol, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
+                               Rm, bad)))
             return r;
-        if ((r = launch_kernel(k_apply_rinv, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
-                               Yin, N, l, rs, (const double*)Rinv, 0, (const float*)nullptr, Q1, (int64_t)0)))
+        if ((r = launch_kernel(k_apply_r, rows_grid(N), dim3(256), 0, st, nullptr, nullptr, Yin, N, l, rs,
+                               (const double*)Rm, 0, (const float*)nullptr, Q1, (int64_t)0)))
             return r;
         if ((r = launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, (const float*)Q1, N,
                                l, (const float*)nullptr, Gp)))
             return r;
-        if ((r = launch_kernel(k_chol_inv, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp,
-                               (int)nch, l, Rinv, bad + 1)))
+        if ((r = launch_kernel(k_chol, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
+                               Rm, bad + 1)))
             return r;
         if (qrow != nullptr &&
-            (r = launch_kernel(k_apply_rinv, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
-                               (const float*)Q1, N, l, (const float*)nullptr, (const double*)Rinv, 0,
-                               (const float*)nullptr, qrow, (int64_t)0)))
+            (r = launch_kernel(k_apply_r, rows_grid(N), dim3(256), 0, st, nullptr, nullptr, (const float*)Q1, N, l,
+                               (const float*)nullptr, (const double*)Rm, 0, (const float*)nullptr, qrow,
+                               (int64_t)0)))
             return r;
-        return launch_kernel(k_apply_rinv, dim3((unsigned)((ldo + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
-                             (const float*)Q1, N, l, (const float*)nullptr, (const double*)Rinv, 1, cs, op, ldo);
+        return launch_kernel(k_apply_r, rows_grid(ldo), dim3(256), 0, st, nullptr, nullptr, (const float*)Q1, N, l,
+                             (const float*)nullptr, (const double*)Rm, 1, cs, op, ldo);
     };
     // Y = W (Om diag(s))^T;  Q = orth(Y) as the [l][M32] operand of W^T Q.
     TTQ_F(launch_kernel(k_scale_cols, dim3((unsigned)(((int64_t)l * K + 255) / 256)), dim3(256), 0, st, nullptr,
@@ -370,10 +377,13 @@ hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, 
     TTQ_F(launch_lowrank_z(Wt, false, K, M32, M32, op, l, Y, st, {}));
     const unsigned nch = (unsigned)((K + kGramRows - 1) / kGramRows);
     TTQ_F(launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, (const float*)Y, K, l, s, Gp));
-    TTQ_F(launch_kernel(k_jacobi, dim3(1), dim3(64), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l, sig, U));
-    TTQ_F(launch_kernel(k_form_b, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
+    TTQ_F(launch_kernel(k_gram_reduce, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
+                        Gm));
+    TTQ_F(launch_kernel(k_jacobi, dim3(1), dim3(jacobi_threads(l)), 0, st, nullptr, nullptr, (const double*)Gm, l,
+                        sig, U));
+    TTQ_F(launch_kernel(k_form_b, dim3((unsigned)((M * rank + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
                         (const float*)Qrow, M, l, rank, (const double*)U, (const double*)sig, B));
-    TTQ_F(launch_kernel(k_form_a, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
+    TTQ_F(launch_kernel(k_form_a, dim3((unsigned)((K * rank + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
                         (const float*)Y, K, l, rank, (const double*)U, (const double*)sig, A));
 #undef TTQ_F
     return hipSuccess;
