@@ -166,6 +166,27 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
                      void* stream);
 
 /*
+ * ttq_qgemm_batched — one decode step of P prompts in one launch.
+ * [TTQ §method b7] the quantized projection, for several prompts at once:
+ * every prompt has its own quantized state (its own s, codes, steps and
+ * zeros: TTQ quantizes per prompt), so this is P independent projections
+ * sharing one launch.  Prompt p uses
+ *   X + p*x_stride ([T][K], stride ldx, elements of xt), s + p*s_stride,
+ *   codes + p*codes_stride (int32 words), scale_f16/zero_f16 + p*sz_stride,
+ *   Y + p*y_stride ([T][M], stride ldy, elements of yt),
+ * and gets exactly what ttq_qgemm gives for it alone (the same kernel, bit
+ * for bit).  1 <= T <= 4, K a multiple of 128, 1 <= P <= 65535; strides
+ * >= 0, keeping every prompt's X, s and codes 16-byte aligned; prompts'
+ * X and Y regions must not overlap.  No workspace.
+ */
+ttq_status ttq_qgemm_batched(const void* X, int xt, int64_t P, int64_t T, int64_t K, int64_t ldx,
+                             int64_t x_stride, const float* s, int64_t s_stride,
+                             const int32_t* codes, int64_t codes_stride,
+                             const uint16_t* scale_f16, const uint16_t* zero_f16, int64_t sz_stride,
+                             int64_t M, int bits, int group, void* Y, int yt, int64_t ldy,
+                             int64_t y_stride, void* stream);
+
+/*
  * ttq_lowrank_add — Y += B (A X), the dynamic low-rank term.
  * [TTQ §method b5]: W = W_q + B A, so the layer adds B (A X) to the
  * quantized projection.  Computed in fp32: Z[t][k] = sum_j A[k][j] X[t][j],

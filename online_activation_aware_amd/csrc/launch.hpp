@@ -73,12 +73,18 @@ hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
                             StageTimer tm = {}, const LowrankEpilogue* lr = nullptr);
 // Few-token projection (decode steps and short prompts): T <= kQgemvMaxT,
-// K a multiple of 128 and at most 16384.
+// K a multiple of 128 (at most 16384 for T > 4).  A batch of P prompts
+// (T <= 4 only) reads prompt p's operands at the element strides of bt.
 constexpr int64_t kQgemvMaxT = 128;
+constexpr int64_t kQgemvBatchMaxT = 4;
+struct QgemvBatch {
+    int64_t x = 0, s = 0, codes = 0, sz = 0, y = 0;
+};
 bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32);
 hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
                         const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
-                        int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm = {});
+                        int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm = {},
+                        int64_t P = 1, QgemvBatch bt = {});
 // Z = X A^T (fp32, [T][rank]) on the matrix cores, for bf16 X, K % 32 == 0
 // and a 16-byte-aligned A.
 bool lowrank_z_mfma_ok(bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A);

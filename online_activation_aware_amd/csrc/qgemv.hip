@@ -279,11 +279,13 @@ struct RowField {
     uint16_t dh[SG], zh[SG];
 };
 
+// Prompt p = blockIdx.y of a batched call reads X + p * x, s + p * s, ...
+// (element strides; all zero for one prompt).
 template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
 __global__ __launch_bounds__(kTMaxWaves * kWave) void k_qgemv_t(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
-    const uint16_t* __restrict__ zero, int64_t M, void* __restrict__ Y, int64_t ldy) {
+    const uint16_t* __restrict__ zero, int64_t M, void* __restrict__ Y, int64_t ldy, QgemvBatch bt) {
     constexpr int RW = trows(TT);
     constexpr int D = tdepth(TT);
     constexpr int SG = GROUP < kTChan ? kTChan / GROUP : 1;   // groups per lane field
@@ -297,6 +299,15 @@ __global__ __launch_bounds__(kTMaxWaves * kWave) void k_qgemv_t(
     const int64_t o0 = (int64_t)blockIdx.x * RW;
     const int64_t wpr = K * BITS / 32, gpr = K / GROUP;
     const int64_t npieces = (K + kTPiece - 1) / kTPiece;
+    {
+        const int64_t pb = blockIdx.y;
+        X = XF32 ? (const void*)((const float*)X + pb * bt.x) : (const void*)((const uint16_t*)X + pb * bt.x);
+        s += pb * bt.s;
+        codes += pb * bt.codes;
+        scale += pb * bt.sz;
+        zero += pb * bt.sz;
+        Y = YF32 ? (void*)((float*)Y + pb * bt.y) : (void*)((uint16_t*)Y + pb * bt.y);
+    }
 
     float acc[RW][TT];
 #pragma unroll
@@ -447,13 +458,13 @@ __global__ __launch_bounds__(kTMaxWaves * kWave) void k_qgemv_t(
 template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
 static hipError_t launch_t(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
                            const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, void* Y,
-                           int64_t ldy, hipStream_t st, StageTimer tm) {
+                           int64_t ldy, hipStream_t st, StageTimer tm, int64_t P, const QgemvBatch& bt) {
     const int64_t np = (K + kTPiece - 1) / kTPiece;
     const int64_t rounds = (np + kTMaxWaves - 1) / kTMaxWaves;
     const int ns = (int)((np + rounds - 1) / rounds);           // waves, each taking `rounds` pieces
-    const dim3 grid((unsigned)((M + trows(TT) - 1) / trows(TT)));
+    const dim3 grid((unsigned)((M + trows(TT) - 1) / trows(TT)), (unsigned)P);
     return launch_kernel(k_qgemv_t<BITS, GROUP, XF32, YF32, TT>, grid, dim3(ns * kWave), 0, st, tm.start, tm.stop,
-                         X, T, K, ldx, s, codes, scale, zero, M, Y, ldy);
+                         X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, bt);
 }
 
 // T <= 4 runs k_qgemv_t (64-bit addressing, any K).  Above that, token rows
@@ -468,10 +479,14 @@ bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32) {
 template <int BITS, int GROUP, bool XF32, bool YF32>
 static hipError_t launch_v4(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
                             const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M,
-                            void* Y, int64_t ldy, hipStream_t st, StageTimer tm) {
-    if (T == 1) return launch_t<BITS, GROUP, XF32, YF32, 1>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
-    if (T == 2) return launch_t<BITS, GROUP, XF32, YF32, 2>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
-    if (T <= 4) return launch_t<BITS, GROUP, XF32, YF32, 4>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
+                            void* Y, int64_t ldy, hipStream_t st, StageTimer tm, int64_t P, const QgemvBatch& bt) {
+    if (T == 1)
+        return launch_t<BITS, GROUP, XF32, YF32, 1>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
+    if (T == 2)
+        return launch_t<BITS, GROUP, XF32, YF32, 2>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
+    if (T <= 4)
+        return launch_t<BITS, GROUP, XF32, YF32, 4>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
+    if (P != 1) return hipErrorInvalidValue;      // batched calls are for T <= 4
     const dim3 grid((unsigned)((M + 15) / 16));
 #define TTQ_V_LAUNCH(NT)                                                                                  \
     return launch_kernel(k_qgemv<BITS, GROUP, XF32, YF32, NT>, grid, dim3(vwaves(NT) * kWave), 0, st,     \
@@ -486,36 +501,39 @@ static hipError_t launch_v4(const void* X, int64_t T, int64_t K, int64_t ldx, co
 template <int BITS, int GROUP>
 static hipError_t launch_v3(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
                             const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M,
-                            void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm) {
+                            void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm, int64_t P,
+                            const QgemvBatch& bt) {
     if (xf32) {
-        if (yf32) return launch_v4<BITS, GROUP, true, true>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
-        return launch_v4<BITS, GROUP, true, false>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
+        if (yf32) return launch_v4<BITS, GROUP, true, true>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
+        return launch_v4<BITS, GROUP, true, false>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
     }
-    if (yf32) return launch_v4<BITS, GROUP, false, true>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
-    return launch_v4<BITS, GROUP, false, false>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm);
+    if (yf32) return launch_v4<BITS, GROUP, false, true>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
+    return launch_v4<BITS, GROUP, false, false>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
 }
 
 template <int BITS>
 static hipError_t launch_v2(int group, const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                             const float* s, const uint32_t* codes, const uint16_t* scale, const uint16_t* zero,
-                            int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm) {
+                            int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm,
+                            int64_t P, const QgemvBatch& bt) {
     switch (group) {
-        case 16: return launch_v3<BITS, 16>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 32: return launch_v3<BITS, 32>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 64: return launch_v3<BITS, 64>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 128: return launch_v3<BITS, 128>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
+        case 16: return launch_v3<BITS, 16>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 32: return launch_v3<BITS, 32>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 64: return launch_v3<BITS, 64>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 128: return launch_v3<BITS, 128>(X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
                         const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
-                        int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm) {
+                        int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm, int64_t P,
+                        QgemvBatch bt) {
     switch (bits) {
-        case 2: return launch_v2<2>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 3: return launch_v2<3>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 4: return launch_v2<4>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
-        case 5: return launch_v2<5>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm);
+        case 2: return launch_v2<2>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 3: return launch_v2<3>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 4: return launch_v2<4>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
+        case 5: return launch_v2<5>(group, X, xf32, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, st, tm, P, bt);
     }
     return hipErrorInvalidValue;
 }

@@ -284,6 +284,35 @@ ttq_status ttq_lowrank_factors(const void* W, int wt, int64_t M, int64_t K, int6
                          "ttq_lowrank_factors launch");
 }
 
+ttq_status ttq_qgemm_batched(const void* X, int xt, int64_t P, int64_t T, int64_t K, int64_t ldx,
+                             int64_t x_stride, const float* s, int64_t s_stride, const int32_t* codes,
+                             int64_t codes_stride, const uint16_t* scale_f16, const uint16_t* zero_f16,
+                             int64_t sz_stride, int64_t M, int bits, int group, void* Y, int yt, int64_t ldy,
+                             int64_t y_stride, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(P >= 1 && P <= 65535, "P (prompts) must be in [1, 65535]");
+    TTQ_REQUIRE(T >= 1 && T <= ttq::kQgemvBatchMaxT, "T must be in [1, %d] for batched decode steps",
+                (int)ttq::kQgemvBatchMaxT);
+    if (ttq_status e = check_quant_shape(M, K, bits, group)) return e;
+    TTQ_REQUIRE(K % 128 == 0, "K must be a multiple of 128");
+    if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
+    if (ttq_status e = check_output(Y, yt, T, M, ldy)) return e;
+    if (M == 0) return TTQ_OK;
+    if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
+    const int64_t xe = esize(xt);
+    TTQ_REQUIRE(x_stride >= 0 && (x_stride * xe) % 16 == 0 && (P == 1 || x_stride >= (T - 1) * ldx + K),
+                "x_stride: negative, not a multiple of 16 bytes, or overlapping prompts");
+    TTQ_REQUIRE(s_stride >= 0 && s_stride % 4 == 0, "s_stride: negative or not a multiple of 16 bytes");
+    TTQ_REQUIRE(codes_stride >= 0 && codes_stride % 4 == 0, "codes_stride: negative or not a multiple of 16 bytes");
+    TTQ_REQUIRE(sz_stride >= 0, "sz_stride: negative");
+    TTQ_REQUIRE(y_stride >= 0 && (P == 1 || y_stride >= (T - 1) * ldy + M), "y_stride: negative or overlapping prompts");
+    ttq::QgemvBatch bt;
+    bt.x = x_stride; bt.s = s_stride; bt.codes = codes_stride; bt.sz = sz_stride; bt.y = y_stride;
+    return device_status(ttq::launch_qgemv(X, xt == TTQ_F32, T, K, ldx, s, (const uint32_t*)codes, scale_f16, zero_f16,
+                                           M, bits, group, Y, yt == TTQ_F32, ldy, as_stream(stream), {}, P, bt),
+                         "ttq_qgemm_batched launch");
+}
+
 ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, const float* A,
                            const float* B, int64_t M, int rank, void* Y, int yt, int64_t ldy, void* ws,
                            size_t ws_bytes, void* stream) {

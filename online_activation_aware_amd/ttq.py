@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttq.so"
 TTQ_OK, TTQ_ERR_INVALID, TTQ_ERR_UNSUPPORTED, TTQ_ERR_DEVICE = 0, 1, 2, 3
 TTQ_F32, TTQ_BF16 = 0, 1
 
-EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm",
+EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm", "ttq_qgemm_batched",
            "ttq_lowrank_add", "ttq_lowrank_factors", "ttq_lowrank_factors_workspace_bytes",
            "ttq_workspace_bytes", "ttq_linear", "ttq_status_str", "ttq_last_error")
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         "ttq_quantize_groups": [vp, i32, i64, i64, i64, vp, i32, i32, vp, vp, i32, vp, vp, vp, vp],
         "ttq_qgemm": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, i32, i64, vp, sz, vp],
         "ttq_lowrank_add": [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, i32, i64, vp, sz, vp],
+        "ttq_qgemm_batched": [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, vp,
+                              i32, i64, i64, vp],
         "ttq_workspace_bytes": [i64, i64, i64, i32, i32, i32],
         "ttq_lowrank_factors": [vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
         "ttq_lowrank_factors_workspace_bytes": [i64, i64, i32],
@@ -204,6 +206,29 @@ def ttq_qgemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: 
                            _dev(codes, "codes"), _dev(scale_f16, "scale_f16"), _dev(zero_f16, "zero_f16"),
                            M, bits, group, _dev(Y, "Y"), _dtype_code(Y), _ld(Y, "Y"), wp, wn,
                            _stream(stream)))
+    return Y
+
+
+def ttq_qgemm_batched(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: torch.Tensor,
+                      zero_f16: torch.Tensor, M: int, bits: int, group: int, Y: Optional[torch.Tensor] = None,
+                      y_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """One decode step of P prompts: X [P][T][K], s [P][K], codes [P][M][.],
+    scale_f16 / zero_f16 [P][M][K/group]; returns Y [P][T][M]."""
+    P, T, K = X.shape
+    if Y is None:
+        Y = torch.empty((P, T, M), dtype=y_dtype, device=X.device)
+    for name, t in (("s", s), ("codes", codes), ("scale_f16", scale_f16), ("zero_f16", zero_f16)):
+        if t.shape[0] != P or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous [P][...] tensor")
+    if X.stride(2) != 1 or Y.stride(2) != 1:
+        raise ValueError("X and Y rows must be contiguous")
+    if scale_f16.stride(0) != zero_f16.stride(0):
+        raise ValueError("scale_f16 and zero_f16 must have the same prompt stride")
+    _check(lib().ttq_qgemm_batched(_dev(X, "X"), _dtype_code(X), P, T, K, X.stride(1), X.stride(0),
+                                   _dev(s, "s"), s.stride(0), _dev(codes, "codes"), codes.stride(0),
+                                   _dev(scale_f16, "scale_f16"), _dev(zero_f16, "zero_f16"), scale_f16.stride(0),
+                                   M, bits, group, _dev(Y, "Y"), _dtype_code(Y), Y.stride(1), Y.stride(0),
+                                   _stream(stream)))
     return Y
 
 

@@ -187,3 +187,22 @@ def test_lowrank_factors_rejects(L):
     assert "workspace" in _err(L)
     assert L.ttq_lowrank_factors_workspace_bytes(256, 512, 24) > 256 * 512 * 2
     assert L.ttq_lowrank_factors_workspace_bytes(256, 512, 40) == 0
+
+
+def test_qgemm_batched_rejects(L):
+    f = L.ttq_qgemm_batched
+    ok = dict(X=FAKE, xt=1, P=3, T=1, K=1024, ldx=1024, xs=1024, s=FAKE, ss=1024, c=FAKE, cst=512, sc=FAKE,
+              z=FAKE, szs=32, M=64, bits=4, group=32, Y=FAKE, yt=0, ldy=64, ys=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["X"], a["xt"], a["P"], a["T"], a["K"], a["ldx"], a["xs"], a["s"], a["ss"], a["c"], a["cst"],
+                 a["sc"], a["z"], a["szs"], a["M"], a["bits"], a["group"], a["Y"], a["yt"], a["ldy"], a["ys"], None)
+    assert call(T=5) == 1 and call(T=0) == 1             # batched steps: 1 <= T <= 4
+    assert call(P=0) == 1
+    assert call(K=1056, ldx=1056, xs=1056) == 1          # K % 128
+    assert call(xs=1000) == 1                            # prompts' X overlap
+    assert call(xs=1028) == 1                            # X stride not 16-byte aligned for bf16
+    assert call(ss=2) == 1 and call(cst=6) == 1          # s / codes strides break 16-byte alignment
+    assert call(ys=10) == 1                              # prompts' Y overlap
+    assert call(s=None) == 1

@@ -253,6 +253,31 @@ def test_qgemv_few_tokens(T, Tn, bits, group, K):
         assert err < 2e-5, (xdt, err)
 
 
+@pytest.mark.parametrize("Tn", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits,group,xdt", [(4, 32, "bf16"), (3, 16, "bf16"), (2, 64, "f32")])
+def test_qgemm_batched_prompts(T, Tn, bits, group, xdt):
+    # One launch for several prompts, each with its own quantized state: every
+    # prompt's Y matches the oracle and, bit for bit, its own ttq_qgemm call.
+    say(f"qgemm batched P=5 T={Tn} bits={bits} group={group} {xdt}")
+    P, K, M = 5, 1152, 203
+    key = "c1" if xdt == "f32" else "c2"
+    Xs, ss, cs, ds, zs, refs = [], [], [], [], [], []
+    for pi in range(P):
+        wl, d = _inputs(key, seed=100 + pi, T=Tn, K=K, M=M)
+        sp = oracle.awq_scales(oracle.stats(d["X"], xdt), Tn, 0.5, 1e-2)
+        r = oracle.group_rtn(oracle.quant_values(d["W"], wl.wdtype, sp), bits, group)
+        refs.append(oracle.project(d["X"], xdt, sp, oracle.dequant(r["q"], r["delta"], r["zero"], group)))
+        Xs.append(to_dev(d["X"], xdt)); ss.append(f32_dev(sp)); cs.append(i32_dev(oracle.pack_codes(r["q"], bits)))
+        ds.append(f16_dev(r["delta"])); zs.append(f16_dev(r["zero"]))
+    Y = T.ttq_qgemm_batched(torch.stack(Xs), torch.stack(ss), torch.stack(cs), torch.stack(ds), torch.stack(zs),
+                            M, bits, group)
+    Yh = host(Y)
+    for pi in range(P):
+        assert rel_fro(Yh[pi], refs[pi]) < 2e-5
+        one = T.ttq_qgemm(Xs[pi], ss[pi], cs[pi], ds[pi], zs[pi], M, bits, group)
+        np.testing.assert_array_equal(host(one), Yh[pi])
+
+
 def test_qgemm_identity_input_layout(T):
     # X = I: Y[t][o] = bf16((q - z) * step / s_t), element by element.
     say("qgemm identity layout")
