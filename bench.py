@@ -334,6 +334,45 @@ def main(argv=None) -> int:
             log(f"  decode T={td:<3d} {us:8.2f} us  {decode[str(td)]['gbs']:8.1f} GB/s "
                 f"({nst} rotating state copies, graph of {nst} steps x {reps})")
 
+        # One decode token for each of P prompts (each with its own quantized
+        # state) in one ttq_qgemm_batched launch, over rotating groups.
+        P = 8
+        ngr = max(2, min(8, math.ceil((args.min_rotation_mib << 20) / (P * sbytes))))
+        groups = [{k: torch.stack([st[k].clone() for _ in range(P)]) for k in ("s", "codes", "scale_f16", "zero_f16")}
+                  for _ in range(ngr)]
+        Xb = to_dev(data["X_decode"][1], wl.xdtype).unsqueeze(0).repeat(P, 1, 1).contiguous()
+        Yb = torch.empty((P, 1, wl.M), dtype=torch.float32, device=dev)
+
+        def bsteps():
+            for g in groups:
+                ttq.ttq_qgemm_batched(Xb, g["s"], g["codes"], g["scale_f16"], g["zero_f16"], wl.M, wl.bits,
+                                      wl.group, Y=Yb)
+        bsteps()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            bsteps()
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(args.steps / ngr))
+        graph.replay()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record()
+        for _ in range(reps):
+            graph.replay()
+        f1.record()
+        torch.cuda.synchronize()
+        us = f0.elapsed_time(f1) / (reps * ngr) * 1e3
+        b = P * (sbytes + wl.K * 4 + wl.K * esize(wl.xdtype) + wl.M * 4)
+        decode["batched_P8_T1"] = {"us": round(us, 2), "prompts": P, "alg_bytes": b,
+                                   "gbs": round(b / (us * 1e-6) / 1e9, 1),
+                                   "hbm_frac": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "tokens_per_s": round(P / (us * 1e-6), 1)}
+        log(f"  decode P={P} prompts x T=1 {us:8.2f} us  {decode['batched_P8_T1']['gbs']:8.1f} GB/s "
+            f"({ngr} rotating groups)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same layer ...")
