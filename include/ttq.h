@@ -273,6 +273,27 @@ typedef struct ttq_linear_args {
 
 ttq_status ttq_linear(const ttq_linear_args* args, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * ttq_linear_shared — several layers that read the same X (q, k and v; gate
+ * and up), with one statistics pass for all of them.
+ * [TTQ §method b3]: the statistics are those of the layer input X, so
+ * projections of the same input share them (and hence lambda and s).
+ *   layers[0..n-1], 1 <= n <= 64: ttq_linear arguments that agree in X, xt,
+ *   T, K, ldx, alpha, lambda_rel and p; M, W, bits, group, the low-rank
+ *   factors, Y and the state outputs are per layer.  The statistics are
+ *   reduced once (into layers[0].ssq if given; every other ssq must be
+ *   NULL), then each layer runs the quantizer and projection of ttq_linear
+ *   in order, with results bitwise equal to separate ttq_linear calls.
+ *   stage_events must be NULL.  ws: ttq_linear_shared_workspace_bytes(
+ *   layers, n) bytes (the statistics plus the largest layer's state and
+ *   scratch; layers run one after another on the stream and reuse it).
+ */
+ttq_status ttq_linear_shared(const ttq_linear_args* layers, int n, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Workspace bytes for ttq_linear_shared (0 when some layer's sizes are not accepted). */
+size_t ttq_linear_shared_workspace_bytes(const ttq_linear_args* layers, int n);
+
 /* Static text for a status code. */
 const char* ttq_status_str(int status);
 

@@ -329,8 +329,7 @@ ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t 
                          "ttq_lowrank_add launch");
 }
 
-ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void* stream) {
-    g_last_error.clear();
+static ttq_status check_linear(const ttq_linear_args* a) {
     TTQ_REQUIRE(a != nullptr, "args: null pointer");
     TTQ_REQUIRE(dim_ok(a->T), "T out of range");
     if (ttq_status e = check_quant_shape(a->M, a->K, a->bits, a->group)) return e;
@@ -349,41 +348,42 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     if (a->stage_events != nullptr)
         for (int i = 0; i < TTQ_LINEAR_STAGE_EVENTS; ++i)
             TTQ_REQUIRE(a->stage_events[i] != nullptr, "stage_events[%d]: null handle", i);
-    if (a->T == 0) return TTQ_OK;   // no prompt tokens: nothing to estimate or project
+    return TTQ_OK;
+}
 
-    const StateLayout L = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank);
-    if (ttq_status e = check_ws(ws, ws_bytes, L.total)) return e;
-    char* w = (char*)ws;
-    double* ssq = a->ssq ? a->ssq : (double*)(w + L.ssq);
-    float* s = a->s ? a->s : (float*)(w + L.s);
-    int32_t* codes = a->codes ? a->codes : (int32_t*)(w + L.codes);
-    uint16_t* scale = a->scale_f16 ? a->scale_f16 : (uint16_t*)(w + L.scale);
-    uint16_t* zero = a->zero_f16 ? a->zero_f16 : (uint16_t*)(w + L.zero);
-    void* scratch = w + L.scratch;
-    hipStream_t st = as_stream(stream);
-    const bool xf32 = a->xt == TTQ_F32;
-
-    // Stage i is timed by events (2i, 2i+1), stamped by the stage's first and
-    // last kernel; a stage that launches nothing records both as markers.
-    void* const* ev = a->stage_events;
-    auto timer = [&](int i) -> ttq::StageTimer {
+// Stage i of ttq_linear is timed by events (2i, 2i+1), stamped by the
+// stage's first and last kernel; a stage that launches nothing records both
+// on the stream as markers.
+struct StageMarks {
+    void* const* ev;
+    hipStream_t st;
+    ttq::StageTimer timer(int i) const {
         if (ev == nullptr) return {};
         return {(hipEvent_t)ev[2 * i], (hipEvent_t)ev[2 * i + 1]};
-    };
-    auto markers = [&](int i) -> ttq_status {
+    }
+    ttq_status markers(int i) const {
         if (ev == nullptr) return TTQ_OK;
         for (int k = 0; k < 2; ++k)
             if (ttq_status e = device_status(hipEventRecord((hipEvent_t)ev[2 * i + k], st), "stage event"))
                 return e;
         return TTQ_OK;
-    };
-    // Statistics (sums of |x|^p); the reduction also leaves the 64-channel
-    // block sums of c.
-    double* bsum = (double*)(w + L.bsum);
-    if (ttq_status e = device_status(ttq::launch_stats(a->X, xf32, a->T, a->K, a->ldx, ssq, 0, (double*)scratch,
-                                                       st, bsum, timer(0), (double)a->p),
-                                     "stats"))
-        return e;
+    }
+};
+
+// Everything after the statistics (ssq, and the block sums of c in bsum):
+// scales, quantizer, projection and low-rank term, with the state and
+// scratch regions of L in w.
+static ttq_status linear_layer(const ttq_linear_args* a, const double* ssq, const double* bsum, char* w,
+                               const StateLayout& L, hipStream_t st) {
+    float* s = a->s ? a->s : (float*)(w + L.s);
+    int32_t* codes = a->codes ? a->codes : (int32_t*)(w + L.codes);
+    uint16_t* scale = a->scale_f16 ? a->scale_f16 : (uint16_t*)(w + L.scale);
+    uint16_t* zero = a->zero_f16 ? a->zero_f16 : (uint16_t*)(w + L.zero);
+    void* scratch = w + L.scratch;
+    const bool xf32 = a->xt == TTQ_F32;
+    const StageMarks sm{a->stage_events, st};
+    auto timer = [&](int i) { return sm.timer(i); };
+    auto markers = [&](int i) { return sm.markers(i); };
     if (a->M == 0) {
         // No rows to quantize: the scales still form part of the prompt state.
         if (ttq_status e = device_status(ttq::launch_awq_scales(ssq, a->T, a->K, a->alpha, a->lambda_rel, a->p, s, st),
@@ -443,6 +443,80 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
                                                  a->yt == TTQ_F32, a->ldy, (float*)scratch, st, timer(3)),
                              "lowrank");
     return markers(3);
+}
+
+ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (ttq_status e = check_linear(a)) return e;
+    if (a->T == 0) return TTQ_OK;   // no prompt tokens: nothing to estimate or project
+    const StateLayout L = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank);
+    if (ttq_status e = check_ws(ws, ws_bytes, L.total)) return e;
+    char* w = (char*)ws;
+    double* ssq = a->ssq ? a->ssq : (double*)(w + L.ssq);
+    double* bsum = (double*)(w + L.bsum);
+    hipStream_t st = as_stream(stream);
+    // Statistics (sums of |x|^p); the reduction also leaves the 64-channel
+    // block sums of c.
+    const StageMarks sm{a->stage_events, st};
+    if (ttq_status e = device_status(ttq::launch_stats(a->X, a->xt == TTQ_F32, a->T, a->K, a->ldx, ssq, 0,
+                                                       (double*)(w + L.scratch), st, bsum, sm.timer(0),
+                                                       (double)a->p),
+                                     "stats"))
+        return e;
+    return linear_layer(a, ssq, bsum, w, L, st);
+}
+
+// Shared statistics: [ssq K fp64 | block sums] at the head of the workspace,
+// then one layer's state and scratch at a time (layers run in order).
+static size_t shared_head(int64_t K) { return round_up((size_t)K * 8) + round_up((size_t)((K + 63) / 64) * 8); }
+
+size_t ttq_linear_shared_workspace_bytes(const ttq_linear_args* layers, int n) {
+    if (layers == nullptr || n < 1) return 0;
+    size_t mx = 0;
+    for (int i = 0; i < n; ++i) {
+        const ttq_linear_args* a = &layers[i];
+        if (ttq_workspace_bytes(a->T, a->K, a->M, a->bits, a->group, a->rank) == 0) return 0;
+        const size_t t = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank).total;
+        if (t > mx) mx = t;
+    }
+    return shared_head(layers[0].K) + mx;
+}
+
+ttq_status ttq_linear_shared(const ttq_linear_args* layers, int n, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    TTQ_REQUIRE(layers != nullptr && n >= 1 && n <= 64, "layers: null, or n not in [1, 64]");
+    const ttq_linear_args* a0 = &layers[0];
+    for (int i = 0; i < n; ++i) {
+        const ttq_linear_args* a = &layers[i];
+        if (ttq_status e = check_linear(a)) return e;
+        TTQ_REQUIRE(a->X == a0->X && a->xt == a0->xt && a->T == a0->T && a->K == a0->K && a->ldx == a0->ldx,
+                    "layer %d: X, xt, T, K and ldx must equal layer 0's (one shared input)", i);
+        TTQ_REQUIRE(a->alpha == a0->alpha && a->lambda_rel == a0->lambda_rel && a->p == a0->p,
+                    "layer %d: alpha, lambda_rel and p must equal layer 0's", i);
+        TTQ_REQUIRE(a->stage_events == nullptr, "layer %d: stage events are not recorded for shared layers", i);
+        TTQ_REQUIRE(i == 0 || a->ssq == nullptr, "layer %d: only layer 0 receives the shared statistics", i);
+    }
+    if (a0->T == 0) return TTQ_OK;
+    const size_t need = ttq_linear_shared_workspace_bytes(layers, n);
+    TTQ_REQUIRE(need > 0, "sizes not accepted");
+    if (ttq_status e = check_ws(ws, ws_bytes, need)) return e;
+    char* w = (char*)ws;
+    const size_t head = shared_head(a0->K);
+    double* ssq = a0->ssq ? a0->ssq : (double*)w;
+    double* bsum = (double*)(w + round_up((size_t)a0->K * 8));
+    char* wl = w + head;
+    hipStream_t st = as_stream(stream);
+    const StateLayout L0 = state_layout(a0->T, a0->K, a0->M, a0->bits, a0->group, a0->rank);
+    if (ttq_status e = device_status(ttq::launch_stats(a0->X, a0->xt == TTQ_F32, a0->T, a0->K, a0->ldx, ssq, 0,
+                                                       (double*)(wl + L0.scratch), st, bsum, {}, (double)a0->p),
+                                     "stats"))
+        return e;
+    for (int i = 0; i < n; ++i) {
+        const ttq_linear_args* a = &layers[i];
+        const StateLayout L = state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank);
+        if (ttq_status e = linear_layer(a, ssq, bsum, wl, L, st)) return e;
+    }
+    return TTQ_OK;
 }
 
 }  // extern "C"

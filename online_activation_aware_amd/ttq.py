@@ -20,7 +20,8 @@ TTQ_F32, TTQ_BF16 = 0, 1
 
 EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm", "ttq_qgemm_batched",
            "ttq_lowrank_add", "ttq_lowrank_factors", "ttq_lowrank_factors_workspace_bytes",
-           "ttq_workspace_bytes", "ttq_linear", "ttq_status_str", "ttq_last_error")
+           "ttq_workspace_bytes", "ttq_linear", "ttq_linear_shared", "ttq_linear_shared_workspace_bytes",
+           "ttq_status_str", "ttq_last_error")
 
 
 class TTQError(RuntimeError):
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         "ttq_lowrank_factors": [vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
         "ttq_lowrank_factors_workspace_bytes": [i64, i64, i32],
         "ttq_linear": [ctypes.POINTER(LinearArgs), vp, sz, vp],
+        "ttq_linear_shared": [ctypes.POINTER(LinearArgs), i32, vp, sz, vp],
+        "ttq_linear_shared_workspace_bytes": [ctypes.POINTER(LinearArgs), i32],
         "ttq_status_str": [i32],
         "ttq_last_error": [],
     }
@@ -79,6 +82,7 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.ttq_workspace_bytes.restype = ctypes.c_size_t
     L.ttq_lowrank_factors_workspace_bytes.restype = ctypes.c_size_t
+    L.ttq_linear_shared_workspace_bytes.restype = ctypes.c_size_t
     L.ttq_status_str.restype = ctypes.c_char_p
     L.ttq_last_error.restype = ctypes.c_char_p
     _lib_handle = L
@@ -296,6 +300,43 @@ def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: f
     wp, wn = _ws(ws, X.device)
     _check(lib().ttq_linear(ctypes.byref(a), wp, wn, _stream(stream)))
     return Y
+
+
+def ttq_linear_shared(X: torch.Tensor, layers: list, alpha: float, lambda_rel: float, p: float = 2.0,
+                      ws: Optional[torch.Tensor] = None, stream=None) -> list:
+    """Several layers on the same X with one statistics pass.  ``layers``:
+    dicts with ``W``, ``bits``, ``group`` and optionally ``B``, ``A``, ``Y``,
+    ``y_dtype``, ``state`` (only the first layer's state may hold ``ssq``).
+    Returns the layers' outputs Y."""
+    T, K = X.shape
+    arr = (LinearArgs * len(layers))()
+    outs = []
+    for i, ly in enumerate(layers):
+        W = ly["W"]
+        M = W.shape[0]
+        B, A = ly.get("B"), ly.get("A")
+        Y = ly.get("Y")
+        if Y is None:
+            Y = torch.empty((T, M), dtype=ly.get("y_dtype", torch.float32), device=X.device)
+        outs.append(Y)
+        st = ly.get("state") or {}
+        arr[i] = LinearArgs(
+            X=_dev(X, "X"), xt=_dtype_code(X), T=T, K=K, ldx=_ld(X, "X"),
+            W=_dev(W, "W"), wt=_dtype_code(W), M=M, ldw=_ld(W, "W"),
+            alpha=alpha, lambda_rel=lambda_rel, p=p, bits=ly["bits"], group=ly["group"],
+            B=_dev(B, "B"), A=_dev(A, "A"), rank=0 if B is None else B.shape[1],
+            Y=_dev(Y, "Y"), yt=_dtype_code(Y), ldy=_ld(Y, "Y"),
+            ssq=_dev(st.get("ssq"), "ssq"), s=_dev(st.get("s"), "s"), codes=_dev(st.get("codes"), "codes"),
+            scale_f16=_dev(st.get("scale_f16"), "scale_f16"), zero_f16=_dev(st.get("zero_f16"), "zero_f16"),
+            stage_events=None)
+    if ws is None:
+        n = lib().ttq_linear_shared_workspace_bytes(arr, len(layers))
+        if n == 0:
+            raise ValueError("no call accepts these sizes")
+        ws = torch.empty(n, dtype=torch.uint8, device=X.device)
+    wp, wn = _ws(ws, X.device)
+    _check(lib().ttq_linear_shared(arr, len(layers), wp, wn, _stream(stream)))
+    return outs
 
 
 TTQ_LINEAR_STAGE_EVENTS = 8

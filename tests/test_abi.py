@@ -206,3 +206,25 @@ def test_qgemm_batched_rejects(L):
     assert call(ss=2) == 1 and call(cst=6) == 1          # s / codes strides break 16-byte alignment
     assert call(ys=10) == 1                              # prompts' Y overlap
     assert call(s=None) == 1
+
+
+def test_linear_shared_rejects(L):
+    from online_activation_aware_amd import ttq
+    arr = (ttq.LinearArgs * 2)()
+    for i in range(2):
+        arr[i] = ttq.LinearArgs(X=FAKE, xt=1, T=8, K=256, ldx=256, W=FAKE, wt=1, M=64, ldw=256, alpha=0.5,
+                                lambda_rel=0.01, p=2.0, bits=4, group=32, B=None, A=None, rank=0, Y=FAKE, yt=0,
+                                ldy=64)
+    assert L.ttq_linear_shared(arr, 0, FAKE, 1 << 30, None) == 1          # n
+    assert L.ttq_linear_shared_workspace_bytes(arr, 2) > 0
+    arr[1].ldx = 512
+    assert L.ttq_linear_shared(arr, 2, FAKE, 1 << 30, None) == 1          # different input
+    assert "layer 1" in _err(L)
+    arr[1].ldx = 256
+    arr[1].alpha = 0.25
+    assert L.ttq_linear_shared(arr, 2, FAKE, 1 << 30, None) == 1          # different alpha
+    arr[1].alpha = 0.5
+    arr[1].ssq = FAKE
+    assert L.ttq_linear_shared(arr, 2, FAKE, 1 << 30, None) == 1          # ssq only on layer 0
+    arr[1].ssq = None
+    assert L.ttq_linear_shared(arr, 2, FAKE, 64, None) == 1               # workspace too small

@@ -400,6 +400,36 @@ def test_linear_moment_p(T, p, key, sizes):
     np.testing.assert_array_equal(host(s2), s)
 
 
+@pytest.mark.parametrize("key,sizes", [("c2", dict(T=300, K=1024)), ("c1", dict(T=96, K=768))])
+def test_linear_shared_statistics(T, key, sizes):
+    # q/k/v-like layers on one X: one statistics pass, then each layer; every
+    # output and state equals its own ttq_linear call bit for bit, and Y
+    # matches the oracle.
+    say(f"linear shared {key} {sizes}")
+    wl, d = _inputs(key, M=256, **sizes)
+    rng = np.random.default_rng(77)
+    shapes = [(256, 4, 32), (128, 3, 16), (192, 2, 64)]
+    X = to_dev(d["X"], wl.xdtype)
+    Ws = [synth.encode(rng.standard_normal((m, wl.K)) * 0.02, wl.wdtype) for m, _, _ in shapes]
+    layers, refs = [], []
+    for (m, b, g), Wh in zip(shapes, Ws):
+        st = T.linear_state(wl.T, wl.K, m, b, g)
+        if layers:
+            st["ssq"] = None
+        layers.append(dict(W=to_dev(Wh, wl.wdtype), bits=b, group=g, state=st))
+        refs.append(oracle.linear(d["X"], wl.xdtype, Wh, wl.wdtype, b, g, wl.alpha, wl.lambda_rel))
+    Ys = T.ttq_linear_shared(X, layers, wl.alpha, wl.lambda_rel)
+    tol = Y_TOL if wl.xdtype == "bf16" else 1e-4
+    for (m, b, g), ly, Y, ref in zip(shapes, layers, Ys, refs):
+        assert rel_fro(host(Y), ref["Y"]) < tol
+        st1 = T.linear_state(wl.T, wl.K, m, b, g)
+        Y1 = T.ttq_linear(X, ly["W"], b, g, wl.alpha, wl.lambda_rel, state=st1)
+        np.testing.assert_array_equal(host(Y1), host(Y))
+        for k in ("s", "codes", "scale_f16", "zero_f16"):
+            np.testing.assert_array_equal(host(st1[k]), host(ly["state"][k]))
+    np.testing.assert_allclose(host(layers[0]["state"]["ssq"]), refs[0]["ssq"], rtol=1e-12)
+
+
 def test_linear_lowrank_unaligned_factor(T):
     # Prompt-sized T with an A that is not 16-byte aligned: the low-rank term
     # is added by the standalone kernels after the GEMM instead of its epilogue.
