@@ -62,6 +62,53 @@ __device__ __forceinline__ uint32_t code_at(const CodeWords<BITS>& c, int i) {
     return v & ((1u << BITS) - 1);
 }
 
+constexpr int kTChan = 32;                        // channels per lane field
+
+template <int N>
+__device__ __forceinline__ float cvt_ubyte(uint32_t v) {
+    float f;
+    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+    return f;
+}
+
+// The 32 codes of a lane's field as fp32 values, code i at bits BITS*i of the
+// little-endian bit stream.
+template <int BITS>
+__device__ __forceinline__ void field_codes(const CodeWords<BITS>& c, float (&q)[kTChan]) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = c.w[i] & 0x0F0F0F0Fu, hi = (c.w[i] >> 4) & 0x0F0F0F0Fu;
+            q[8 * i + 0] = cvt_ubyte<0>(lo);
+            q[8 * i + 1] = cvt_ubyte<0>(hi);
+            q[8 * i + 2] = cvt_ubyte<1>(lo);
+            q[8 * i + 3] = cvt_ubyte<1>(hi);
+            q[8 * i + 4] = cvt_ubyte<2>(lo);
+            q[8 * i + 5] = cvt_ubyte<2>(hi);
+            q[8 * i + 6] = cvt_ubyte<3>(lo);
+            q[8 * i + 7] = cvt_ubyte<3>(hi);
+        }
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t m = (c.w[i] >> (2 * j)) & 0x03030303u;   // codes 4 b + j of this word
+                q[16 * i + j] = cvt_ubyte<0>(m);
+                q[16 * i + 4 + j] = cvt_ubyte<1>(m);
+                q[16 * i + 8 + j] = cvt_ubyte<2>(m);
+                q[16 * i + 12 + j] = cvt_ubyte<3>(m);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTChan; ++i) q[i] = (float)code_at<BITS>(c, i);
+    }
+}
+
 template <int BITS, int GROUP, bool XF32, bool YF32, int NT>
 __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
@@ -119,20 +166,32 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
             if (c >= nchunks) break;                  // wave-uniform
             const int64_t k0 = c * kVChunk + 32 * q;
             // Expand the lane's 32 weights into 4 MFMA operands (hi/lo for fp32 X).
+            // (q - z) * step = fma(q, step, -z * step) exactly (small integers
+            // times an fp16 step), then times 1/s.  Rows >= M read row o0 and
+            // their outputs are never stored.
+            // The first token tile's operands (bf16 X) are requested before the
+            // weights are expanded, so that the expansion covers their latency.
+            u32x4 xb0[4];
+            if constexpr (!XF32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xb0[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rx, (int)((r * ldx + k0 + 8 * j) * esz), 0, 0));
+            }
             u32x4 ah[4], al[4];
+            float qall[kTChan];
+            field_codes<BITS>(cw[p], qall);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int gsel = GROUP < 32 ? (8 * j) / GROUP : 0;
-                const float df = f16_to_f32(dh[p][gsel]), zf = f16_to_f32(zh[p][gsel]);
+                const float df = f16_to_f32(dh[p][gsel]);
+                const float nzd = -f16_to_f32(zh[p][gsel]) * df;
                 const f32x4 i0 = *(const f32x4*)(sinv + k0 + 8 * j);
                 const f32x4 i1 = *(const f32x4*)(sinv + k0 + 8 * j + 4);
                 const float inv[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
                 float w[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float qv = (float)code_at<BITS>(cw[p], 8 * j + e);
-                    w[e] = ((qv - zf) * df) * inv[e];
-                }
+                for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf(qall[8 * j + e], df, nzd) * inv[e];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     ah[j][e] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
@@ -142,10 +201,6 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
                         al[j][e] = pack_bf16x2(r0, r1);
                     }
                 }
-            }
-            if (!orow) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ah[j] = al[j] = u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -173,7 +228,9 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
                         acc[n] = mfma_16x16x32(ah[j], bl, acc[n]);
                         acc[n] = mfma_16x16x32(al[j], bh, acc[n]);
                     } else {
-                        const u32x4 xb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0));
+                        const u32x4 xb = n == 0 ? xb0[j]
+                                                : __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                                rx, voff, 0, 0));
                         acc[n] = mfma_16x16x32(ah[j], xb, acc[n]);
                     }
                 }
@@ -222,56 +279,10 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
 // computes, so each load instruction reads a contiguous b x 256-byte run of
 // one row.  Per-lane sums are added over the wave by a fixed butterfly and
 // over the waves in wave order (deterministic).
-constexpr int kTChan = 32;                        // channels per lane
 constexpr int kTPiece = kTChan * kWave;           // channels per piece
 constexpr int kTMaxWaves = 8;
 constexpr int trows(int tt) { return tt == 4 ? 8 : 16; }   // rows per workgroup
 constexpr int tdepth(int tt) { return tt == 1 ? 3 : 2; }                  // rows in flight per wave
-
-template <int N>
-__device__ __forceinline__ float cvt_ubyte(uint32_t v) {
-    float f;
-    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
-    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
-    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
-    return f;
-}
-
-// The 32 codes of a lane's field as fp32 values, code i at bits BITS*i of the
-// little-endian bit stream.
-template <int BITS>
-__device__ __forceinline__ void field_codes(const CodeWords<BITS>& c, float (&q)[kTChan]) {
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = c.w[i] & 0x0F0F0F0Fu, hi = (c.w[i] >> 4) & 0x0F0F0F0Fu;
-            q[8 * i + 0] = cvt_ubyte<0>(lo);
-            q[8 * i + 1] = cvt_ubyte<0>(hi);
-            q[8 * i + 2] = cvt_ubyte<1>(lo);
-            q[8 * i + 3] = cvt_ubyte<1>(hi);
-            q[8 * i + 4] = cvt_ubyte<2>(lo);
-            q[8 * i + 5] = cvt_ubyte<2>(hi);
-            q[8 * i + 6] = cvt_ubyte<3>(lo);
-            q[8 * i + 7] = cvt_ubyte<3>(hi);
-        }
-    } else if constexpr (BITS == 2) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t m = (c.w[i] >> (2 * j)) & 0x03030303u;   // codes 4 b + j of this word
-                q[16 * i + j] = cvt_ubyte<0>(m);
-                q[16 * i + 4 + j] = cvt_ubyte<1>(m);
-                q[16 * i + 8 + j] = cvt_ubyte<2>(m);
-                q[16 * i + 12 + j] = cvt_ubyte<3>(m);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kTChan; ++i) q[i] = (float)code_at<BITS>(c, i);
-    }
-}
 
 template <int BITS, int SG>
 struct RowField {
