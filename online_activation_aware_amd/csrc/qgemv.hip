@@ -125,6 +125,13 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
     const int64_t o0 = (int64_t)blockIdx.x * 16;
     const int64_t o = o0 + r;
     const bool orow = o < M;
+    {
+        // Token block blockIdx.y: tokens 16 NT y .. 16 NT y + 16 NT - 1.
+        const int64_t tb = (int64_t)blockIdx.y * NT * 16;
+        X = XF32 ? (const void*)((const float*)X + tb * ldx) : (const void*)((const uint16_t*)X + tb * ldx);
+        Y = YF32 ? (void*)((float*)Y + tb * ldy) : (void*)((uint16_t*)Y + tb * ldy);
+        T = T - tb < (int64_t)NT * 16 ? T - tb : (int64_t)NT * 16;
+    }
 
     // 1/s by v_rcp_f32, as in the other projection kernels.
     for (int64_t j = threadIdx.x; j < K; j += kVThreads) sinv[j] = __builtin_amdgcn_rcpf(s[j]);
@@ -498,13 +505,19 @@ static hipError_t launch_v4(const void* X, int64_t T, int64_t K, int64_t ldx, co
     if (T <= 4)
         return launch_t<BITS, GROUP, XF32, YF32, 4>(X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, st, tm, P, bt);
     if (P != 1) return hipErrorInvalidValue;      // batched calls are for T <= 4
-    const dim3 grid((unsigned)((M + 15) / 16));
+    // Token tiles per workgroup: all of them, unless the row blocks alone
+    // would leave most compute units idle; then the tiles are split over a
+    // second grid dimension (each such workgroup expands its rows' weights).
+    const int64_t gx = (M + 15) / 16;
+    int nt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
+    while (nt > 1 && gx * ((T + 16 * nt - 1) / (16 * nt)) < 256) nt /= 2;
+    const dim3 grid((unsigned)gx, (unsigned)((T + 16 * nt - 1) / (16 * nt)));
 #define TTQ_V_LAUNCH(NT)                                                                                  \
     return launch_kernel(k_qgemv<BITS, GROUP, XF32, YF32, NT>, grid, dim3(vwaves(NT) * kWave), 0, st,     \
                          tm.start, tm.stop, X, T, K, ldx, s, codes, scale, zero, M, Y, ldy)
-    if (T <= 16) TTQ_V_LAUNCH(1);
-    if (T <= 32) TTQ_V_LAUNCH(2);
-    if (T <= 64) TTQ_V_LAUNCH(4);
+    if (nt == 1) TTQ_V_LAUNCH(1);
+    if (nt == 2) TTQ_V_LAUNCH(2);
+    if (nt == 4) TTQ_V_LAUNCH(4);
     TTQ_V_LAUNCH(8);
 #undef TTQ_V_LAUNCH
 }
