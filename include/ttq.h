@@ -155,8 +155,12 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  *   multiplied by a matrix-core GEMM; otherwise codes are dequantized tile
  *   by tile inside the GEMM kernel.  The last three see bitwise the same
  *   bf16 weights.
- *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (M*K*2
- *   rounded up to 256 when T >= 192, none otherwise); only read and written
+ *   For bf16 X with 12 <= T <= 16 the expansion runs split over K (each
+ *   workgroup: 64 rows, one K slice; fp32 partials in ws, added in slice
+ *   order by a second kernel).
+ *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (the
+ *   split partials, S*T*M*4 for S <= K/128 slices, when 12 <= T <= 16; M*K*2
+ *   when T >= 192; rounded up to 256; none otherwise); only read and written
  *   by the kernels this call enqueues.
  */
 ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,

@@ -81,6 +81,14 @@ struct QgemvBatch {
     int64_t x = 0, s = 0, codes = 0, sz = 0, y = 0;
 };
 bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32);
+// kSkMinT <= T <= 16, bf16 X, K a multiple of 128: split-K variant with an
+// fp32 partial workspace P of qgemv_sk_ws_bytes(T, K, M) bytes.
+constexpr int64_t kSkMinT = 12;
+bool qgemv_sk_eligible(int64_t T, int64_t K, int64_t ldx, bool xf32);
+size_t qgemv_sk_ws_bytes(int64_t T, int64_t K, int64_t M);
+hipError_t launch_qgemv_sk(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
+                           const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
+                           int group, void* Y, bool yf32, int64_t ldy, float* P, hipStream_t st, StageTimer tm = {});
 hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
                         const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
                         int group, void* Y, bool yf32, int64_t ldy, hipStream_t st, StageTimer tm = {},

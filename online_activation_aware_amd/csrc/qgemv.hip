@@ -485,6 +485,228 @@ static hipError_t launch_t(const void* X, int64_t T, int64_t K, int64_t ldx, con
                          X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, bt);
 }
 
+// ---------------------------------------------------------------------------
+// 12 <= T <= 16 with a workspace: split K.  A workgroup owns 64 output rows
+// (four MFMA row tiles) and one of KS slices of K.  Its 16 waves take the
+// slice's 128-channel chunks in turn; per chunk a wave requests the codes of
+// all four row tiles and the token fragments, then expands the tiles one by
+// one (as k_qgemv: the same bf16 w/s per weight) into four accumulators, so
+// each token fragment read from L2 serves 64 rows instead of 16.  The wave
+// tiles are added in wave order and the workgroup's fp32 partial goes to
+// P[ks][T][M]; k_sk_reduce adds the KS partials in slice order.
+constexpr int kSkTiles = 4;                       // 16-row MFMA tiles per workgroup
+constexpr int kSkWaves = 16;
+constexpr int64_t kSkMaxSlice = 8192;             // channels per slice (1/s staged in LDS)
+
+template <int BITS, int GROUP, bool XF32>
+__global__ __launch_bounds__(kSkWaves * kWave) void k_qgemv_sk(
+    const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+    const uint16_t* __restrict__ zero, int64_t M, int64_t kslice, float* __restrict__ P) {
+    constexpr int G2 = GROUP < 32 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) float sinv[kSkMaxSlice];
+    __shared__ f32x4 red[kSkWaves][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t o0 = (int64_t)blockIdx.x * 16 * kSkTiles;
+    const int64_t ks = blockIdx.y;
+    const int64_t kbeg = ks * kslice;
+    const int64_t kend = kbeg + kslice < K ? kbeg + kslice : K;
+
+    for (int64_t j = threadIdx.x; j < kend - kbeg; j += kSkWaves * kWave)
+        sinv[j] = __builtin_amdgcn_rcpf(s[kbeg + j]);
+
+    const int64_t wpr = K * BITS / 32, gpr = K / GROUP;
+    const uint32_t* crow[kSkTiles];
+    const uint16_t* srow[kSkTiles];
+    const uint16_t* zrow[kSkTiles];
+#pragma unroll
+    for (int rt = 0; rt < kSkTiles; ++rt) {
+        int64_t o = o0 + 16 * rt + r;
+        if (o >= M) o = M - 1;                    // rows past M: loads stay in bounds, outputs unused
+        crow[rt] = codes + o * wpr;
+        srow[rt] = scale + o * gpr;
+        zrow[rt] = zero + o * gpr;
+    }
+    const int64_t esz = XF32 ? 4 : 2;
+    const rsrc_t rx = make_rsrc(X, ((T - 1) * ldx + K) * esz);   // tokens >= T read as zero
+
+    f32x4 acc[kSkTiles];
+#pragma unroll
+    for (int rt = 0; rt < kSkTiles; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    const int64_t nch = (kend - kbeg) / kVChunk;
+    for (int64_t c = wave; c < nch; c += kSkWaves) {
+        const int64_t kl = c * kVChunk + 32 * q;  // channel within the slice
+        const int64_t k0 = kbeg + kl;
+        CodeWords<BITS> cw[kSkTiles];
+        uint16_t dh[kSkTiles][G2], zh[kSkTiles][G2];
+#pragma unroll
+        for (int rt = 0; rt < kSkTiles; ++rt) {
+            load_codes<BITS>(cw[rt], crow[rt] + k0 * BITS / 32);
+#pragma unroll
+            for (int h = 0; h < G2; ++h) {
+                dh[rt][h] = srow[rt][k0 / GROUP + h];
+                zh[rt][h] = zrow[rt][k0 / GROUP + h];
+            }
+        }
+        // Token fragments of this chunk (bf16 hi [+ lo for fp32 X]).
+        u32x4 bh[4], bl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int voff = (int)((r * ldx + k0 + 8 * j) * esz);
+            if constexpr (XF32) {
+                const f32x4 xa = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0));
+                const f32x4 xc = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + 16, 0, 0));
+                const float xv[8] = {xa[0], xa[1], xa[2], xa[3], xc[0], xc[1], xc[2], xc[3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bh[j][e] = pack_bf16x2(xv[2 * e], xv[2 * e + 1]);
+                    bl[j][e] = pack_bf16x2(xv[2 * e] - bf16lo_to_f32(bh[j][e]), xv[2 * e + 1] - bf16hi_to_f32(bh[j][e]));
+                }
+            } else {
+                bh[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < kSkTiles; ++rt) {
+            float qall[kTChan];
+            field_codes<BITS>(cw[rt], qall);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int gsel = GROUP < 32 ? (8 * j) / GROUP : 0;
+                const float df = f16_to_f32(dh[rt][gsel]);
+                const float nzd = -f16_to_f32(zh[rt][gsel]) * df;
+                const f32x4 i0 = *(const f32x4*)(sinv + kl + 8 * j);
+                const f32x4 i1 = *(const f32x4*)(sinv + kl + 8 * j + 4);
+                const float inv[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
+                u32x4 ah, al;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float w0 = __builtin_fmaf(qall[8 * j + 2 * e], df, nzd) * inv[2 * e];
+                    const float w1 = __builtin_fmaf(qall[8 * j + 2 * e + 1], df, nzd) * inv[2 * e + 1];
+                    ah[e] = pack_bf16x2(w0, w1);
+                    if constexpr (XF32) al[e] = pack_bf16x2(w0 - bf16lo_to_f32(ah[e]), w1 - bf16hi_to_f32(ah[e]));
+                }
+                acc[rt] = mfma_16x16x32(ah, bh[j], acc[rt]);
+                if constexpr (XF32) {
+                    acc[rt] = mfma_16x16x32(ah, bl[j], acc[rt]);
+                    acc[rt] = mfma_16x16x32(al, bh[j], acc[rt]);
+                }
+            }
+        }
+    }
+
+    // Lane holds Y^T[o0 + 16 rt + 4 q + i][r] for tile rt; the 16 wave tiles
+    // are added in wave order by one wave per row tile.
+    float* Pk = P + ks * T * M;
+#pragma unroll
+    for (int rt = 0; rt < kSkTiles; ++rt) {
+        if (rt > 0) __syncthreads();
+        red[wave][lane] = acc[rt];
+        __syncthreads();
+        if (wave == rt) {
+            f32x4 sum = red[0][lane];
+            for (int w = 1; w < kSkWaves; ++w) {
+                const f32x4 v = red[w][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum[i] += v[i];
+            }
+            const int64_t ob = o0 + 16 * rt + 4 * q;
+            if (r < T)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (ob + i < M) Pk[(int64_t)r * M + ob + i] = sum[i];
+        }
+    }
+}
+
+// Y[t][o] = sum over slices ks = 0.. of P[ks][t][o], in slice order.
+template <bool YF32>
+__global__ __launch_bounds__(256) void k_sk_reduce(const float* __restrict__ P, int ksn, int64_t T, int64_t M,
+                                                   void* __restrict__ Y, int64_t ldy) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * M) return;
+    const int64_t t = idx / M, o = idx % M;
+    float a = P[idx];
+    for (int k = 1; k < ksn; ++k) a += P[(int64_t)k * T * M + idx];
+    if constexpr (YF32) ((float*)Y)[t * ldy + o] = a;
+    else ((uint16_t*)Y)[t * ldy + o] = (uint16_t)f32_to_bf16(a);
+}
+
+// Slices for the split-K path: enough workgroups to fill the chip, each
+// slice a whole number of chunks and at most kSkMaxSlice channels.
+int64_t qgemv_sk_slices(int64_t K, int64_t M) {
+    const int64_t gx = (M + 16 * kSkTiles - 1) / (16 * kSkTiles);
+    const int64_t nch = K / kVChunk;
+    int64_t ks = (256 + gx - 1) / gx;
+    if (ks > nch) ks = nch;
+    while ((nch + ks - 1) / ks * kVChunk > kSkMaxSlice) ++ks;
+    return ks < 1 ? 1 : ks;
+}
+
+// bf16 X only (with fp32 X the three-product expansion does not fit the
+// registers of 16 waves), and T >= 12: below that the second launch costs
+// about what the shared token fragments save (measured: T = 5 and 8 equal or
+// slower, T = 16 29.1 -> 26.0 us on the 14336 -> 4096 layer).
+bool qgemv_sk_eligible(int64_t T, int64_t K, int64_t ldx, bool xf32) {
+    return !xf32 && T >= kSkMinT && T <= 16 && K % kVChunk == 0 && (int64_t)16 * ldx * 2 < ((int64_t)1 << 31);
+}
+
+size_t qgemv_sk_ws_bytes(int64_t T, int64_t K, int64_t M) {
+    return (size_t)qgemv_sk_slices(K, M) * (size_t)T * (size_t)M * sizeof(float);
+}
+
+template <int BITS, int GROUP, bool XF32>
+static hipError_t launch_sk3(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s, const uint32_t* codes,
+                             const uint16_t* scale, const uint16_t* zero, int64_t M, void* Y, bool yf32, int64_t ldy,
+                             float* P, hipStream_t st, StageTimer tm) {
+    const int64_t ksn = qgemv_sk_slices(K, M);
+    const int64_t nch = K / kVChunk;
+    const int64_t kslice = (nch + ksn - 1) / ksn * kVChunk;
+    const int64_t ksr = (K + kslice - 1) / kslice;             // slices actually used
+    const dim3 grid((unsigned)((M + 16 * kSkTiles - 1) / (16 * kSkTiles)), (unsigned)ksr);
+    if (hipError_t e = launch_kernel(k_qgemv_sk<BITS, GROUP, XF32>, grid, dim3(kSkWaves * kWave), 0, st, tm.start,
+                                     nullptr, X, T, K, ldx, s, codes, scale, zero, M, kslice, P))
+        return e;
+    const dim3 g2((unsigned)((T * M + 255) / 256));
+    return yf32 ? launch_kernel(k_sk_reduce<true>, g2, dim3(256), 0, st, nullptr, tm.stop, (const float*)P, (int)ksr,
+                                T, M, Y, ldy)
+                : launch_kernel(k_sk_reduce<false>, g2, dim3(256), 0, st, nullptr, tm.stop, (const float*)P,
+                                (int)ksr, T, M, Y, ldy);
+}
+
+template <int BITS>
+static hipError_t launch_sk2(int group, bool xf32, const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
+                             const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, void* Y,
+                             bool yf32, int64_t ldy, float* P, hipStream_t st, StageTimer tm) {
+#define TTQ_SK(G) return launch_sk3<BITS, G, false>(X, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, P, st, tm)
+    switch (group) {
+        case 16: TTQ_SK(16);
+        case 32: TTQ_SK(32);
+        case 64: TTQ_SK(64);
+        case 128: TTQ_SK(128);
+    }
+#undef TTQ_SK
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_qgemv_sk(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
+                           const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
+                           int group, void* Y, bool yf32, int64_t ldy, float* P, hipStream_t st, StageTimer tm) {
+    if (!qgemv_sk_eligible(T, K, ldx, xf32)) return hipErrorInvalidValue;
+    switch (bits) {
+        case 2: return launch_sk2<2>(group, xf32, X, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, P, st, tm);
+        case 3: return launch_sk2<3>(group, xf32, X, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, P, st, tm);
+        case 4: return launch_sk2<4>(group, xf32, X, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, P, st, tm);
+        case 5: return launch_sk2<5>(group, xf32, X, T, K, ldx, s, codes, scale, zero, M, Y, yf32, ldy, P, st, tm);
+    }
+    return hipErrorInvalidValue;
+}
+
 // T <= 4 runs k_qgemv_t (64-bit addressing, any K).  Above that, token rows
 // up to 127 are addressed (padded tiles read as zero) with 32-bit buffer
 // offsets, and 1/s of every channel is staged in LDS.

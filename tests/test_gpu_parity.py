@@ -224,7 +224,7 @@ def test_qgemm_ragged_and_bf16_output(T, Tn, M):
         assert rel_fro(got, ref) < tol
 
 
-@pytest.mark.parametrize("Tn", [1, 3, 16, 17, 33, 64, 65, 128])
+@pytest.mark.parametrize("Tn", [1, 3, 5, 8, 12, 16, 17, 33, 64, 65, 128])
 @pytest.mark.parametrize("bits,group", [(4, 32), (3, 16), (2, 64), (5, 128)])
 def test_qgemv_parity(T, Tn, bits, group):
     # The few-token kernel (T <= 128, K % 128 == 0): K = 1152 gives the 16
