@@ -288,8 +288,10 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
 // over the waves in wave order (deterministic).
 constexpr int kTPiece = kTChan * kWave;           // channels per piece
 constexpr int kTMaxWaves = 8;
-constexpr int trows(int tt) { return tt == 4 ? 8 : 16; }   // rows per workgroup
-constexpr int tdepth(int tt) { return tt == 1 ? 3 : 2; }                  // rows in flight per wave
+// 16 rows per workgroup: the grid's waves fit the chip in one round.  Rows
+// in flight per wave: 3 for one token, 2 for two, 1 for four (registers).
+constexpr int trows(int tt) { return 16; }
+constexpr int tdepth(int tt) { return tt == 1 ? 3 : tt == 2 ? 2 : 1; }
 
 template <int BITS, int SG>
 struct RowField {
