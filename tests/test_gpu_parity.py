@@ -278,6 +278,31 @@ def test_qgemm_batched_prompts(T, Tn, bits, group, xdt):
         np.testing.assert_array_equal(host(one), Yh[pi])
 
 
+def test_largest_K(T):
+    # K = 2^18, the largest K the library accepts (4096 channel blocks of 64
+    # for the shrinkage mean): statistics, fused scales, quantization and the
+    # projection for one, two and eight tokens.
+    say("largest K = 2^18")
+    K, M = 1 << 18, 16
+    for Tn in (1, 2, 8):
+        wl, d = _inputs("c2", seed=50 + Tn, T=Tn, K=K, M=M)
+        ref = oracle.linear(d["X"], "bf16", d["W"], "bf16", 4, 32, 0.5, 1e-2)
+        Y, st = _run_linear(T, wl, d)
+        np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
+        np.testing.assert_allclose(host(st["s"]), ref["s"], rtol=S_TOL)
+        tol = 2e-5 if Tn <= 4 else Y_TOL
+        assert rel_fro(host(Y), ref["Y"]) < tol
+
+
+@pytest.mark.parametrize("Tn", [8, 12, 16])
+def test_qgemm_few_tokens_beyond_16384_channels(T, Tn):
+    # K above the matrix-core few-token kernel's limit: T = 8 falls back to
+    # the tile kernel, T = 12 and 16 take the split-K path.
+    say(f"qgemm T={Tn} K=18432")
+    got, ref = _qgemm_case(T, "c2", Tn, 18432, 96, 4, 32, "bf16", "f32", seed=Tn)
+    assert rel_fro(got, ref) < Y_TOL
+
+
 def test_qgemm_identity_input_layout(T):
     # X = I: Y[t][o] = bf16((q - z) * step / s_t), element by element.
     say("qgemm identity layout")
