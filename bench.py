@@ -227,7 +227,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # Timed region: K steps back to back, nothing else on the stream.
+    # Timed region (`value`): K steps back to back, each ttq_linear called
+    # from Python, nothing else on the stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -239,6 +240,29 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/layer (wall {wall * 1e3 / args.steps * 1e3:.1f} us/step)")
+
+    # Graph region (reported beside `value`): the same K steps, step i
+    # replaying a HIP graph that holds one ttq_linear call on input copy
+    # i % ncopy.  It shows how much of the eager figure is host launch time.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for c in range(ncopy):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % ncopy].replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % ncopy].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / args.steps
+    log(f"graph replay {args.steps} steps: {graph_ms * 1e3:.1f} us/layer")
 
     # Instrumented region: K more steps in which ttq_linear stamps HIP events
     # with its own kernels' start and end times on the launch stream
@@ -399,6 +423,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": breakdown,
+        "graph_us_per_layer": round(graph_ms * 1e3, 3),
         "decode": decode,
         "factors": factors,
     }

@@ -14,6 +14,9 @@
 // by buffer->LDS DMA into 3-slot rings issued two steps ahead (no staging
 // registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
 // one barrier per 64-deep K step, each wave waiting only for its own DMA.
+// Fragments are double-buffered in registers: the LDS reads of one 32-deep
+// half overlap the MFMAs of the other, and waves raise their issue priority
+// while they feed the matrix cores.
 // Optionally the epilogue adds the low-rank term Z B^T (fp32) before the store.
 #include "common.hpp"
 #include "launch.hpp"
@@ -76,28 +79,42 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         for (int i = 0; i < WOPS; ++i)
             dma_to_lds<16>(rw, wd + (wave * WOPS + i) * 1024, woff0 + i * wrow8, (int)k0 * 2);
     };
-    auto compute = [&](const uint8_t* xs, const uint8_t* ws) __attribute__((always_inline)) {
-        u32x4 a[2][4], b[2][FB];
+    // Fragments of one 32-deep half of a K step: a = 4 row fragments of W~,
+    // b = FB token fragments of X.  Set 0 holds the first half, set 1 the
+    // second, so the matrix cores work on one set while the other is read.
+    u32x4 a0[4], b0[FB], a1[4], b1[FB];
+    auto rd = [&](u32x4* a, u32x4* b, const uint8_t* xs, const uint8_t* ws, int kk) __attribute__((always_inline)) {
+        const int c = 4 * kk + (lane >> 4);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = 4 * kk + (lane >> 4);
+        for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(ws + lds_swz(wm * 64 + 16 * i + (lane & 15), c));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[kk][i] = *(const u32x4*)(ws + lds_swz(wm * 64 + 16 * i + (lane & 15), c));
-#pragma unroll
-            for (int j = 0; j < FB; ++j) b[kk][j] = *(const u32x4*)(xs + lds_swz(wn * WT + 16 * j + (lane & 15), c));
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < FB; ++j) acc[i][j] = mfma_16x16x32(a[kk][i], b[kk][j], acc[i][j]);
+        for (int j = 0; j < FB; ++j) b[j] = *(const u32x4*)(xs + lds_swz(wn * WT + 16 * j + (lane & 15), c));
     };
-    auto step = [&](bool more, const uint8_t* xc, const uint8_t* wc, uint8_t* xn, uint8_t* wn_, int64_t kt)
-        __attribute__((always_inline)) {
+    auto mm = [&](const u32x4* a, const u32x4* b) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < FB; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // Step kt (ring slot xc/wc): its first-half fragments are read while the
+    // previous step's second half runs on the matrix cores; then the DMA two
+    // steps ahead is issued and the second-half fragments are read while the
+    // first half runs.  Every LDS read of the slot has completed before the
+    // closing barrier, so the slot can be refilled one step later, and the
+    // loop iterations begin with no LDS read in flight.
+    auto step = [&](bool first, bool more, const uint8_t* xc, const uint8_t* wc, uint8_t* xn, uint8_t* wn_,
+                    int64_t kt) __attribute__((always_inline)) {
+        rd(a0, b0, xc, wc, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!first) mm(a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
         if (more) issue(xn, wn_, (kt + 2) * kBK);
-        __builtin_amdgcn_sched_barrier(0);        // keep the prefetch ahead of this step's work
-        compute(xc, wc);
+        rd(a1, b1, xc, wc, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
         if (more) wait_vmcnt<OPS>();              // step kt+1's operands have landed
         else wait_vmcnt<0>();
         sync_lds();
@@ -112,17 +129,19 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         wait_vmcnt<0>();
     }
     sync_lds();
-    int64_t kt = 0;
+    step(true, 2 < nk, sX0, sW0, sX2, sW2, 0);
+    int64_t kt = 1;
     for (; kt + 5 <= nk; kt += 3) {
-        step(true, sX0, sW0, sX2, sW2, kt + 0);
-        step(true, sX1, sW1, sX0, sW0, kt + 1);
-        step(true, sX2, sW2, sX1, sW1, kt + 2);
+        step(false, true, sX1, sW1, sX0, sW0, kt + 0);
+        step(false, true, sX2, sW2, sX1, sW1, kt + 1);
+        step(false, true, sX0, sW0, sX2, sW2, kt + 2);
     }
     for (; kt < nk; kt += 3) {
-        step(kt + 2 < nk, sX0, sW0, sX2, sW2, kt + 0);
-        if (kt + 1 < nk) step(kt + 3 < nk, sX1, sW1, sX0, sW0, kt + 1);
-        if (kt + 2 < nk) step(kt + 4 < nk, sX2, sW2, sX1, sW1, kt + 2);
+        step(false, kt + 2 < nk, sX1, sW1, sX0, sW0, kt + 0);
+        if (kt + 1 < nk) step(false, kt + 3 < nk, sX2, sW2, sX1, sW1, kt + 1);
+        if (kt + 2 < nk) step(false, kt + 4 < nk, sX0, sW0, sX2, sW2, kt + 2);
     }
+    mm(a1, b1);
 
     if constexpr (LR) {
         // [TTQ §method b5] low-rank term Y += B (A X) = Z B^T, in fp32, added
