@@ -18,6 +18,8 @@
 // half overlap the MFMAs of the other, and waves raise their issue priority
 // while they feed the matrix cores.
 // Optionally the epilogue adds the low-rank term Z B^T (fp32) before the store.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_dma.hpp"
@@ -32,7 +34,7 @@ template <int BN, bool YF32, bool LR>
 __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const uint16_t* __restrict__ Wq,
     int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec, const float* __restrict__ Z,
-    const float* __restrict__ Bm, int rank) {
+    const float* __restrict__ Bm, int rank, int64_t zstride) {
     constexpr int NW = kBThreads / kWave;                       // 8 waves
     constexpr int WT = BN / 4;                                  // tokens per wave (64 or 32)
     constexpr int FB = WT / 16;                                 // token fragments per wave
@@ -46,6 +48,13 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     __shared__ __attribute__((aligned(1024))) uint8_t sW1[kBM * kBRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t sW2[kBM * kBRowB];
 
+    // Split over K (grid.z > 1): slice z multiplies input channels
+    // [z K, (z + 1) K) and stores its partial product at Y + z zstride.
+    if (gridDim.z > 1) {
+        X += (int64_t)blockIdx.z * K;
+        Wq += (int64_t)blockIdx.z * K;
+        Y = (char*)Y + (int64_t)blockIdx.z * zstride * (YF32 ? 4 : 2);
+    }
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -193,21 +202,75 @@ bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw) {
            (int64_t)kBM * ldw * 2 < ((int64_t)1 << 31);
 }
 
+// Y = P[0] + P[1] + ... (fp32 partial products of the K slices, added in
+// slice order, rows of ldp floats), stored as fp32 or bf16 (RNE).
+template <bool YF32>
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ P, int S, int64_t T, int64_t M,
+                                                   int64_t ldp, int64_t zstride, void* __restrict__ Y, int64_t ldy,
+                                                   int yvec) {
+    const int64_t nq = (M + 3) / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * nq; i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i / nq, o = 4 * (i % nq);
+        f32x4 acc = *(const f32x4*)(P + t * ldp + o);
+        for (int s = 1; s < S; ++s) {
+            const f32x4 v = *(const f32x4*)(P + s * zstride + t * ldp + o);
+            acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+        }
+        store_y4<YF32>(Y, t * ldy + o, M - o, yvec, acc);
+    }
+}
+
+// K slices for a projection whose 128 x 256 tiles alone would leave most
+// compute units idle: two slices of at least 4096 channels each keep the
+// 256-token tiles (and their lower LDS traffic per flop) and double the
+// workgroups; otherwise none (the 128 x 128 tiles are used instead).
+int gemm_bf16_splits(int64_t T, int64_t K, int64_t M) {
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((T + 255) / 256);
+    if (tiles >= 192 || tiles * 2 > 512) return 1;
+    if (K % (2 * kBK) != 0 || K / 2 < 4096) return 1;
+    return 2;
+}
+
+static int64_t split_ld(int64_t M) { return (M + 3) / 4 * 4; }
+
+size_t gemm_bf16_split_ws_bytes(int64_t T, int64_t K, int64_t M) {
+    const int S = gemm_bf16_splits(T, K, M);
+    return S > 1 ? (size_t)S * (size_t)T * (size_t)split_ld(M) * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
-                            StageTimer tm, const LowrankEpilogue* lr) {
+                            StageTimer tm, const LowrankEpilogue* lr, float* split_ws) {
     const int yvec = ((uintptr_t)Y % 16 == 0) && ((ldy * (yf32 ? 4 : 2)) % 16 == 0);
-    // 128 x 256 tiles, unless they would leave most compute units idle; then
-    // 128 x 128 (twice the workgroups).
     const int64_t mt = (M + kBM - 1) / kBM;
-    const bool narrow = mt * ((T + 255) / 256) < 192;
-    const dim3 grid((unsigned)mt, (unsigned)((T + (narrow ? 127 : 255)) / (narrow ? 128 : 256)));
     const float* Z = lr ? lr->Z : nullptr;
     const float* B = lr ? lr->B : nullptr;
     const int rank = lr ? lr->rank : 0;
+    const int S = (lr == nullptr && split_ws != nullptr) ? gemm_bf16_splits(T, K, M) : 1;
+    if (S > 1) {
+        // fp32 partials of the K slices into the workspace (rows of ldp
+        // floats, 16-byte aligned), then their ordered sum into Y.
+        const int64_t ldp = split_ld(M), zs = T * ldp;
+        const dim3 grid((unsigned)mt, (unsigned)((T + 255) / 256), (unsigned)S);
+        hipError_t e = launch_kernel(k_gemm_bf16<256, true, false>, grid, dim3(kBThreads), 0, st, tm.start,
+                                     nullptr, X, T, K / S, ldx, Wq, ldw, M, (void*)split_ws, ldp, 1,
+                                     (const float*)nullptr, (const float*)nullptr, 0, zs);
+        if (e != hipSuccess) return e;
+        const int64_t work = T * ((M + 3) / 4);
+        const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 4096);
+        if (yf32)
+            return launch_kernel(k_split_sum<true>, dim3(blocks), dim3(256), 0, st, nullptr, tm.stop,
+                                 (const float*)split_ws, S, T, M, ldp, zs, Y, ldy, yvec);
+        return launch_kernel(k_split_sum<false>, dim3(blocks), dim3(256), 0, st, nullptr, tm.stop,
+                             (const float*)split_ws, S, T, M, ldp, zs, Y, ldy, yvec);
+    }
+    // 128 x 256 tiles, unless they would leave most compute units idle; then
+    // 128 x 128 (twice the workgroups).
+    const bool narrow = mt * ((T + 255) / 256) < 192;
+    const dim3 grid((unsigned)mt, (unsigned)((T + (narrow ? 127 : 255)) / (narrow ? 128 : 256)));
 #define TTQ_B_LAUNCH(BN, YF, LRF)                                                                          \
     return launch_kernel(k_gemm_bf16<BN, YF, LRF>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, \
-                         ldx, Wq, ldw, M, Y, ldy, yvec, Z, B, rank)
+                         ldx, Wq, ldw, M, Y, ldy, yvec, Z, B, rank, (int64_t)0)
 #define TTQ_B_LAUNCH2(BN)                                 \
     if (rank > 0) {                                       \
         if (yf32) TTQ_B_LAUNCH(BN, true, true);           \

@@ -69,9 +69,22 @@ hipError_t launch_qgemm(const void* X, bool xf32, int64_t T, int64_t K, int64_t 
 // the matrix-core GEMM; smaller ones (and fp32 X) the fused kernel.
 constexpr int64_t kDequantGemmMinT = 192;
 bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw);
+// split_ws (optional, gemm_bf16_split_ws_bytes(T, K, M) bytes, 16-byte
+// aligned): lets a projection with too few 128 x 256 tiles run as two K
+// slices plus an ordered sum (only without the low-rank epilogue).
 hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, const uint16_t* Wq,
                             int64_t ldw, int64_t M, void* Y, bool yf32, int64_t ldy, hipStream_t st,
-                            StageTimer tm = {}, const LowrankEpilogue* lr = nullptr);
+                            StageTimer tm = {}, const LowrankEpilogue* lr = nullptr, float* split_ws = nullptr);
+int gemm_bf16_splits(int64_t T, int64_t K, int64_t M);
+size_t gemm_bf16_split_ws_bytes(int64_t T, int64_t K, int64_t M);
+// Workspace of the prompt-sized projection: the dequantized weight (M x K
+// bf16), then, 256-byte aligned, the K-slice partials.
+inline size_t dequant_ws_bytes(int64_t M, int64_t K) {
+    return ((size_t)M * (size_t)K * 2 + 255) / 256 * 256;
+}
+inline float* split_ws_after(uint16_t* wq, int64_t M, int64_t K) {
+    return wq ? (float*)((char*)wq + dequant_ws_bytes(M, K)) : nullptr;
+}
 // Few-token projection (decode steps and short prompts): T <= kQgemvMaxT,
 // K a multiple of 128 (at most 16384 for T > 4).  A batch of P prompts
 // (T <= 4 only) reads prompt p's operands at the element strides of bt.

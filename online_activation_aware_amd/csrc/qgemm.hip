@@ -253,7 +253,8 @@ static hipError_t launch_g3(const void* X, bool xf32, int64_t T, int64_t K, int6
         if (hipError_t e = launch_kernel(k_dequant<BITS, GROUP>, gd, dim3(256), 0, st, tm.start, nullptr, codes,
                                          scale, zero, s, M, K, wq))
             return e;
-        return launch_gemm_bf16((const uint16_t*)X, T, K, ldx, wq, K, M, Y, yf32, ldy, st, {nullptr, tm.stop});
+        return launch_gemm_bf16((const uint16_t*)X, T, K, ldx, wq, K, M, Y, yf32, ldy, st, {nullptr, tm.stop},
+                                nullptr, split_ws_after(wq, M, K));
     }
     // 4 consecutive outputs are stored as one vector when Y's rows allow it.
     const int yvec = ((uintptr_t)Y % 16 == 0) && ((ldy * (yf32 ? 4 : 2)) % 16 == 0);

@@ -122,7 +122,7 @@ size_t ws_qgemm(int64_t T, int64_t K, int64_t M) {
     // 12 <= T <= 16: fp32 partials of the split-K few-token projection.
     if (T >= ttq::kSkMinT && T <= 16 && K % 128 == 0) return round_up(ttq::qgemv_sk_ws_bytes(T, K, M));
     if (T < ttq::kDequantGemmMinT) return 0;
-    return round_up((size_t)M * (size_t)K * sizeof(uint16_t));
+    return ttq::dequant_ws_bytes(M, K) + round_up(ttq::gemm_bf16_split_ws_bytes(T, K, M));
 }
 bool use_dequant_gemm(int64_t T, bool xf32, int64_t K, int64_t ldx) {
     return !xf32 && T >= ttq::kDequantGemmMinT && ttq::gemm_bf16_supported(T, K, ldx, K);
@@ -441,7 +441,8 @@ static ttq_status linear_layer(const ttq_linear_args* a, const double* ssq, cons
         }
         if (ttq_status e = device_status(ttq::launch_gemm_bf16((const uint16_t*)a->X, a->T, a->K, a->ldx, wq,
                                                                a->K, a->M, a->Y, a->yt == TTQ_F32, a->ldy, st,
-                                                               timer(2), fuse ? &lre : nullptr),
+                                                               timer(2), fuse ? &lre : nullptr,
+                                                               fuse ? nullptr : ttq::split_ws_after(wq, a->M, a->K)),
                                          "gemm"))
             return e;
         if (fuse) return TTQ_OK;

@@ -224,6 +224,16 @@ def test_qgemm_ragged_and_bf16_output(T, Tn, M):
         assert rel_fro(got, ref) < tol
 
 
+@pytest.mark.parametrize("Tn,M", [(300, 130), (600, 1024)])
+def test_qgemm_split_k(T, Tn, M):
+    # ttq_qgemm at prompt-sized T with few output tiles and K = 8192: the
+    # projection runs as two K slices whose fp32 partials are added in order.
+    say(f"qgemm split-K T={Tn} M={M}")
+    for ydt, tol in (("f32", Y_TOL), ("bf16", Y_TOL_BF16_OUT)):
+        got, ref = _qgemm_case(T, "c4", Tn, 8192, M, 4, 32, "bf16", ydt, seed=Tn)
+        assert rel_fro(got, ref) < tol
+
+
 @pytest.mark.parametrize("Tn", [1, 3, 5, 8, 12, 16, 17, 33, 64, 65, 128])
 @pytest.mark.parametrize("bits,group", [(4, 32), (3, 16), (2, 64), (5, 128)])
 def test_qgemv_parity(T, Tn, bits, group):
@@ -364,6 +374,8 @@ E2E = [
     ("c3-long", dict(T=400, K=1024, M=320)),
     ("c4-long", dict(T=256, K=2048, M=256)),
     ("c5-long", dict(T=260, K=512, M=512)),
+    # few 128 x 256 tiles and K >= 8192: two K slices plus their ordered sum
+    ("c4-split", dict(T=260, K=8192, M=302)),
 ]
 
 
@@ -484,12 +496,14 @@ def test_decode_steps_reuse_prompt_state(T):
         assert rel_fro(host(Yd), refd) < Y_TOL, td
 
 
-def test_linear_and_qgemm_share_the_dequantized_weight(T):
+@pytest.mark.parametrize("key,sizes", [("c3", dict(T=384, K=1024, M=320)), ("c4", dict(T=300, K=8192, M=260))])
+def test_linear_and_qgemm_share_the_dequantized_weight(T, key, sizes):
     # For prompt-sized T the whole-layer call takes the dequantized weight
     # from the quantizer, ttq_qgemm expands the stored codes itself; both
-    # must produce the same bf16 weight, hence bitwise the same Y.
-    say("linear vs qgemm on the prompt state")
-    wl, d = _inputs("c3", T=384, K=1024, M=320)
+    # must produce the same bf16 weight, hence bitwise the same Y (the
+    # second shape runs the projection as two K slices).
+    say(f"linear vs qgemm on the prompt state {key} {sizes}")
+    wl, d = _inputs(key, **sizes)
     Y, st = _run_linear(T, wl, d)
     ws = T.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group)
     Yq = T.ttq_qgemm(to_dev(d["X"], "bf16"), st["s"], st["codes"], st["scale_f16"], st["zero_f16"],
