@@ -157,11 +157,14 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  *   bf16 weights.
  *   For bf16 X with 12 <= T <= 16 the expansion runs split over K (each
  *   workgroup: 64 rows, one K slice; fp32 partials in ws, added in slice
- *   order by a second kernel).
+ *   order by a second kernel).  The T >= 192 GEMM also runs as two K slices
+ *   when its 128 x 256 output tiles number fewer than 192 and K >= 8192 (a
+ *   multiple of 128): fp32 partial products in ws, then Y = P0 + P1.
  *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (the
  *   split partials, S*T*M*4 for S <= K/128 slices, when 12 <= T <= 16; M*K*2
- *   when T >= 192; rounded up to 256; none otherwise); only read and written
- *   by the kernels this call enqueues.
+ *   when T >= 192, plus 2*T*M'*4 with M' = M rounded up to 4 when the GEMM
+ *   runs as two K slices; each part rounded up to 256; none otherwise); only
+ *   read and written by the kernels this call enqueues.
  */
 ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
                      const float* s, const int32_t* codes, const uint16_t* scale_f16,
