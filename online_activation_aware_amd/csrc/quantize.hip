@@ -189,7 +189,7 @@ __device__ __forceinline__ void unpack_row(const RawRow<WF32>& r, float (&w)[8])
     }
 }
 
-template <int BITS, int GROUP, bool WF32, bool LOWRANK, bool SFUSE>
+template <int BITS, int GROUP, bool WF32, bool LOWRANK, bool SFUSE, bool RB4>
 __global__ __launch_bounds__(kQThreads) void k_quantize(
     const void* __restrict__ W, int64_t M, int64_t K, int64_t ldw, const float* __restrict__ s,
     const float* __restrict__ B, const float* __restrict__ A, int rank, int rows_per_block,
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     // grid is sized to the number of workgroups the device holds at once),
     // and each wave issues the loads of its next batch before it processes
     // the current one, so loads stay in flight while the VALU works.
-    constexpr int RB = (LOWRANK || WF32) ? 4 : 8;
+    constexpr int RB = (LOWRANK || WF32 || RB4) ? 4 : 8;
     constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
     const int64_t nrb = (M + rows_per_block - 1) / rows_per_block;
     auto load_batch = [&](RawRow<WF32> (&dst)[RB], int64_t rb) __attribute__((always_inline)) {
@@ -347,8 +347,12 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
                             const QScaleSrc* qs, hipStream_t st, StageTimer tm) {
     const bool lr = rank > 0;
     // Rows per block: one batch per wave (4 waves x 8 rows for bf16, x 4 for
-    // fp32 or with low-rank factors).
-    const int rows = (lr || wf32) ? 16 : 32;
+    // fp32 or with low-rank factors).  Large bf16 weights (more than 2^25
+    // values) also take batches of 4 rows: measured faster there (the
+    // 14336 x 4096 layer 64.8 -> 54.4 us, 4096 x 14336 51.7 -> 50.4 us),
+    // slower on 4096 x 4096 (19.9 -> 22.4 us).
+    const bool rb4 = !lr && !wf32 && M * K > ((int64_t)1 << 25);
+    const int rows = (lr || wf32 || rb4) ? 16 : 32;
     const int64_t strips = (K + kQChans - 1) / kQChans;
     const int64_t nrb = (M + rows - 1) / rows;
     const size_t lds = lr ? (size_t)rank * kQChans * sizeof(float) : 0;
@@ -371,19 +375,21 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
         if (gy > 65535) gy = 65535;
         return dim3((unsigned)strips, (unsigned)gy);
     };
-#define TTQ_Q_LAUNCH(WF, LR, SF)                                                                         \
+#define TTQ_Q_LAUNCH(WF, LR, SF, R4)                                                                     \
     do {                                                                                                 \
         static std::atomic<int> occ{0};                                                                  \
-        auto kern = k_quantize<BITS, GROUP, WF, LR, SF>;                                                 \
+        auto kern = k_quantize<BITS, GROUP, WF, LR, SF, R4>;                                             \
         return launch_kernel(kern, grid_for((const void*)kern, occ), dim3(kQThreads), lds, st, tm.start,  \
                              tm.stop, W, M, K, ldw, s, B, A, rank, rows, codes, scale, zero, wq, q);     \
     } while (0)
-#define TTQ_Q_LAUNCH2(WF, LR) \
-    if (qs) TTQ_Q_LAUNCH(WF, LR, true); else TTQ_Q_LAUNCH(WF, LR, false)
+#define TTQ_Q_LAUNCH2(WF, LR, R4) \
+    if (qs) TTQ_Q_LAUNCH(WF, LR, true, R4); else TTQ_Q_LAUNCH(WF, LR, false, R4)
     if (wf32) {
-        if (lr) { TTQ_Q_LAUNCH2(true, true); } else { TTQ_Q_LAUNCH2(true, false); }
+        if (lr) { TTQ_Q_LAUNCH2(true, true, false); } else { TTQ_Q_LAUNCH2(true, false, false); }
     } else {
-        if (lr) { TTQ_Q_LAUNCH2(false, true); } else { TTQ_Q_LAUNCH2(false, false); }
+        if (lr) { TTQ_Q_LAUNCH2(false, true, false); }
+        else if (rb4) { TTQ_Q_LAUNCH2(false, false, true); }
+        else { TTQ_Q_LAUNCH2(false, false, false); }
     }
 
 #undef TTQ_Q_LAUNCH2

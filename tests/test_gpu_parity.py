@@ -144,6 +144,22 @@ def test_quantize_parity(T, wdt, bits, group):
     _check_codes(T, host(codes), r["q"], r["u"], bits, K)
 
 
+@pytest.mark.parametrize("bits,group", [(4, 32), (3, 16)])
+def test_quantize_large_weight(T, bits, group):
+    # More than 2^25 bf16 weights: the quantizer takes 4-row batches; ragged
+    # row count so that the last row block is partial.
+    M, K = 2051, 16384
+    say(f"quantize large M={M} K={K} bits={bits} group={group}")
+    rng = np.random.default_rng(77 + bits)
+    W = synth.encode(rng.standard_normal((M, K), dtype=np.float32) * 0.01, "bf16")
+    s = (rng.lognormal(0, 0.5, K)).astype(np.float32)
+    r = oracle.group_rtn(oracle.quant_values(W, "bf16", s), bits, group)
+    codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "bf16"), f32_dev(s), bits, group)
+    np.testing.assert_array_equal(host(sc), r["delta"])
+    np.testing.assert_array_equal(host(zz), r["zero"])
+    _check_codes(T, host(codes), r["q"], r["u"], bits, K)
+
+
 def test_quantize_without_scales_is_plain_rtn(T):
     say("quantize s=NULL")
     M, K = 64, 512
