@@ -47,7 +47,7 @@ def _check_codes(T, got_codes, or_q, or_u, bits, K):
 # ------------------------------------------------------------------ stats
 
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
-@pytest.mark.parametrize("Tn,K", [(1, 512), (77, 1000), (300, 2056), (1031, 4104)])
+@pytest.mark.parametrize("Tn,K", [(1, 512), (77, 1000), (300, 2056), (1031, 4104), (600, 10304)])
 def test_stats_parity(T, xdt, Tn, K):
     say(f"stats xdt={xdt} T={Tn} K={K}")
     rng = np.random.default_rng(Tn + K)
