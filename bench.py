@@ -122,24 +122,42 @@ def cpu_baseline(wl, data, B=None, A=None) -> dict:
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    times = []
+    times, stages = [], {"stats_scales": [], "quantize": [], "projection": []}
     t_start = time.perf_counter()
     while len(times) < 64 and (len(times) < 3 or time.perf_counter() - t_start < 10.0):
         t0 = time.perf_counter()
         ssq = oracle.stats(data["X"], wl.xdtype)
         s = oracle.awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel)
+        t1 = time.perf_counter()
         v = oracle.quant_values(data["W"], wl.wdtype, s, B, A)
         r = oracle.group_rtn(v, wl.bits, wl.group)
         oracle.pack_codes(r["q"], wl.bits)
+        t2 = time.perf_counter()
         w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], wl.group)
         Y = oracle.project(data["X"], wl.xdtype, s, w_hat, B, A)
-        times.append(time.perf_counter() - t0)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        stages["stats_scales"].append(t1 - t0)
+        stages["quantize"].append(t2 - t1)
+        stages["projection"].append(t3 - t2)
         assert np.isfinite(Y).all()
     dt = float(np.median(times))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count()
     return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
             "sample": f"the full layer ({wl.T}x{wl.K}->{wl.M}) through the fp64 numpy oracle (stats, scales, "
                       f"quantize, pack, dequantize, projection), median of {len(times)} runs "
-                      f"({sum(times):.1f} s of CPU work); cores = BLAS threads"}
+                      f"({sum(times):.1f} s of CPU work); cores = BLAS threads",
+            "stages_us": {k: round(float(np.median(v)) * 1e6, 1) for k, v in stages.items()},
+            "cpu_model": cpu_model, "host_cpus": avail}
 
 
 def main(argv=None) -> int:
@@ -276,6 +294,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     per_step = [e.stage_ms() for e in evs]
     stage_ms = {k: sum(p[k] for p in per_step) / args.steps for k in ttq.LINEAR_STAGES}
+
+    def pct(vals, q):
+        v = sorted(vals)
+        return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
     if not wl.rank:
         stage_ms.pop("lowrank")
 
@@ -301,6 +323,8 @@ def main(argv=None) -> int:
     for name, v in stage_ms.items():
         us = v * 1e3
         d = {"us": round(us, 2)}
+        vals = [p[name] * 1e3 for p in per_step]
+        d["p10_p50_p90_us"] = [round(pct(vals, q), 2) for q in (0.1, 0.5, 0.9)]
         if name in alg:
             d["alg_bytes"] = alg[name]
             d["gbs"] = round(alg[name] / (us * 1e-6) / 1e9, 1)
