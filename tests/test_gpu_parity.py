@@ -99,18 +99,19 @@ def test_scales_zero_input_is_one(T):
 
 @pytest.mark.parametrize("p", [1.0, 3.0, 0.5])
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
-def test_stats_and_scales_moment_p(T, p, xdt):
+@pytest.mark.parametrize("Tn", [300, 200])     # 200: the one-kernel statistics path
+def test_stats_and_scales_moment_p(T, p, xdt, Tn):
     # [TTQ §method b4] p fixed in advance: sums of |x|^p and s = (c + lambda)^(alpha/p).
-    say(f"stats p={p} {xdt}")
+    say(f"stats p={p} {xdt} T={Tn}")
     key = "c1" if xdt == "f32" else "c2"
-    wl, d = _inputs(key, T=300, K=1096)
+    wl, d = _inputs(key, T=Tn, K=1096)
     X = to_dev(d["X"], xdt)
     ws = torch.empty(32 * 1096 * 8, dtype=torch.uint8, device="cuda")   # 32 fp64 partial rows
     msum = T.ttq_stats_p(X, p, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
     ref = oracle.stats(d["X"], xdt, p=p)
     np.testing.assert_allclose(host(msum), ref, rtol=1e-12)
-    s = T.ttq_awq_scales(msum, 300, 0.5, 1e-2, p=p)
-    np.testing.assert_allclose(host(s), oracle.awq_scales(ref, 300, 0.5, 1e-2, p=p), rtol=1e-6)
+    s = T.ttq_awq_scales(msum, Tn, 0.5, 1e-2, p=p)
+    np.testing.assert_allclose(host(s), oracle.awq_scales(ref, Tn, 0.5, 1e-2, p=p), rtol=1e-6)
     # ttq_stats is the p = 2 case
     ssq = T.ttq_stats(X, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
     sq2 = T.ttq_stats_p(X, 2.0, torch.empty(1096, dtype=torch.float64, device="cuda"), ws=ws)
