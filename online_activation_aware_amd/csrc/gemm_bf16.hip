@@ -29,6 +29,7 @@ namespace ttq {
 constexpr int kBM = 128, kBK = 64;            // token tile BN: 256, or 128 for small grids
 constexpr int kBThreads = 512;
 constexpr int kBRowB = kBK * 2;                  // 128-byte LDS rows
+constexpr unsigned kXcds = 8, kXcdRows = 8;     // XCDs; row tiles per XCD block
 
 template <int BN, bool YF32, bool LR>
 __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
@@ -59,8 +60,25 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int wm = wave >> 2, wn = wave & 3;      // 2 x 4 waves of 64 x WT
-    const int64_t o0 = (int64_t)blockIdx.x * kBM;
-    const int64_t t0 = (int64_t)blockIdx.y * BN;
+    // Tile order for the eight XCDs, each with its own L2: workgroups are
+    // dispatched to XCDs round-robin by linear id, so the ids an XCD receives
+    // are mapped to one compact block of 8 row tiles x (token tiles / 2)
+    // instead of every token tile (on the 4096 x 2048 output of a 4096-channel layer each XCD reads
+    // 16.8 MB of operands instead of 21).  Grids that do not divide keep
+    // the plain order.
+    int64_t ob = blockIdx.x, tb = blockIdx.y;
+    {
+        const unsigned mt = gridDim.x, nt = gridDim.y, n = mt * nt;
+        if (n % kXcds == 0 && mt % kXcdRows == 0) {
+            const unsigned b = blockIdx.x + mt * blockIdx.y;
+            const unsigned v = (b % kXcds) * (n / kXcds) + b / kXcds;
+            const unsigned r = v % (kXcdRows * nt);
+            ob = (int64_t)(v / (kXcdRows * nt)) * kXcdRows + r % kXcdRows;
+            tb = r / kXcdRows;
+        }
+    }
+    const int64_t o0 = ob * kBM;
+    const int64_t t0 = tb * BN;
     const int rows_x = (int)min((int64_t)BN, T - t0);
     const int rows_w = (int)min((int64_t)kBM, M - o0);
     const rsrc_t rx = make_rsrc(X + t0 * ldx, ((int64_t)(rows_x - 1) * ldx + K) * 2);
