@@ -56,6 +56,16 @@ def test_workspace_bytes(L):
     assert n >= state + 4096 * 4096 * 2
     assert ttq.ttq_workspace_bytes(16, 4096, 4096, 4, 32, 0) < state + 4096 * 4096 * 2
     assert ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 16) >= ttq.ttq_workspace_bytes(2048, 4096, 4096, 2, 32, 0)
+    # 14336 -> 4096 at T = 1024 has 128 output tiles of 128 x 256: the GEMM
+    # runs as two K slices, whose fp32 partials follow the dequantized weight
+    T, K, M = 1024, 14336, 4096
+    st4 = K * 8 + K * 4 + M * K * 4 // 8 + 2 * M * (K // 32) * 2
+    n4 = ttq.ttq_workspace_bytes(T, K, M, 4, 32, 0)
+    assert n4 >= st4 + M * K * 2 + 2 * T * M * 4
+    # with 256 or more tiles (T = 2048 here) no partials are needed
+    assert ttq.ttq_workspace_bytes(2048, K, M, 4, 32, 0) < st4 + M * K * 2 + 2 * 2048 * M * 4
+    # ragged M: the partial rows are padded to a multiple of 4 floats
+    assert ttq.ttq_workspace_bytes(300, 8192, 130, 4, 32, 0) >= 8192 * 130 * 2 + 2 * 300 * 132 * 4
     for bad in [(10, 100, 10, 4, 32, 0),     # K not a multiple of 32
                 (10, 128, 10, 6, 32, 0),     # bits
                 (10, 128, 10, 4, 48, 0),     # group
