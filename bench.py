@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 # invalidates them (traffic is then reported as null).
 MEASURED_TRAFFIC = {
     # 4096->4096, T=2048 layer: profiles/ttq_linear_4096x4096_t2048_b4g32_pmc_traffic.txt
-    "e28402a6d78cf354": {"workload": "c2", "fetch_bytes": 134381413, "write_bytes": 34970822,
+    "e6ba3bfc58666292": {"workload": "c2", "fetch_bytes": 134381413, "write_bytes": 34970822,
                          "fetch_factor": 1.9999, "write_factor": 1.0},
 }
 
@@ -50,9 +50,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM source's code (comments and blank lines dropped), so
+    that the stored traffic counters go stale when the kernel changes."""
+    import re
     path = os.path.join(ROOT, "online_activation_aware_amd", "csrc", "gemm_bf16.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()[:16]
 
 
 def esize(dt: str) -> int:

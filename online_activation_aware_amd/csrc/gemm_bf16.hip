@@ -8,9 +8,10 @@
 // that of the fused dequantize-in-LDS kernel, so both paths see identical
 // bf16 weights.
 //
-// Tiling: 128 output rows x 256 tokens per workgroup (128 x 128 when the grid
-// would otherwise leave most compute units idle), 8 waves (2 per SIMD), each
-// 64 x 64 (or 64 x 32): 4 x 4 (4 x 2) MFMA 16x16x32 per 32-deep slice.  Both operands arrive
+// Tiling: 128 output rows x 256 tokens per workgroup; when such tiles would
+// leave most compute units idle, two K slices (fp32 partials, then their
+// ordered sum) or 128 x 128 tiles.  8 waves (2 per SIMD), each 64 x 64 (or
+// 64 x 32): 4 x 4 (4 x 2) MFMA 16x16x32 per 32-deep slice.  Both operands arrive
 // by buffer->LDS DMA into 3-slot rings issued two steps ahead (no staging
 // registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
 // one barrier per 64-deep K step, each wave waiting only for its own DMA.
