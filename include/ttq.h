@@ -73,8 +73,8 @@ typedef enum {
  *   X: [T][K] fp32 or bf16 (xt), stride ldx >= K.   ssq: [K] fp64, output.
  *   accumulate != 0 adds to the existing ssq (chunked prefill), else
  *   overwrites it.  ws: scratch for at most 32 fp64 partial rows, i.e.
- *   32*K*8 bytes whatever T is (ttq_workspace_bytes covers it; short
- *   prompts and K >= 10240 take a one-kernel path that leaves it unused);
+ *   32*K*8 bytes whatever T is (ttq_workspace_bytes covers it; T <= 256
+ *   or K > 10176 take a one-kernel path that leaves it unused);
  *   all sums are reduced in a fixed order, so results are bitwise
  *   reproducible run to run.  K must be a multiple of 8.
  */
