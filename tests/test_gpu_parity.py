@@ -266,7 +266,8 @@ def test_qgemv_parity(T, Tn, bits, group):
 
 @pytest.mark.parametrize("Tn", [1, 2, 3, 4])
 @pytest.mark.parametrize("bits,group,K", [(4, 32, 1152), (4, 32, 4224), (3, 16, 4224), (2, 64, 18432),
-                                          (5, 128, 4224), (4, 16, 2048), (2, 128, 1152)])
+                                          (5, 128, 4224), (4, 16, 2048), (2, 128, 1152),
+                                          (4, 32, 14336), (3, 64, 8320)])
 def test_qgemv_few_tokens(T, Tn, bits, group, K):
     # One to four tokens run on the vector ALUs in fp32 (no bf16 rounding of
     # weights or tokens), so the bar is fp32 accumulation, not 2e-3.  K = 1152
