@@ -176,8 +176,11 @@ __global__ __launch_bounds__(256) void k_apply_r(const float* __restrict__ Y, in
 // eigenvectors as columns of U [l][l].
 __global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, int l, double* __restrict__ sig,
                                                  double* __restrict__ U) {
-    __shared__ double a[kFMaxL][kFMaxL + 1];
-    __shared__ double v[kFMaxL][kFMaxL + 1];
+    // Two copies of A and V: a round reads one and writes the other, so it
+    // needs two barriers (rotations known, new values written) instead of a
+    // third one before overwriting in place.
+    __shared__ double a[2][kFMaxL][kFMaxL + 1];
+    __shared__ double v[2][kFMaxL][kFMaxL + 1];
     __shared__ double rc[kFMaxL], rs_[kFMaxL];
     __shared__ int ptn[kFMaxL];
     __shared__ double wsum[16];
@@ -187,15 +190,16 @@ __global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, i
     const bool in = tid < l * l;
     const int n = l + (l & 1);                    // even count for the pairing (a dummy index if odd)
     if (in) {
-        a[i][j] = G[i * l + j];
-        v[i][j] = (i == j) ? 1.0 : 0.0;
+        a[0][i][j] = G[i * l + j];
+        v[0][i][j] = (i == j) ? 1.0 : 0.0;
     }
     __syncthreads();
+    int cur = 0;
     double scale = 0.0;
-    for (int k = 0; k < l; ++k) scale += a[k][k];
+    for (int k = 0; k < l; ++k) scale += a[0][k][k];
     for (int sweep = 0; sweep < 30; ++sweep) {
         // Off-diagonal mass, reduced over the block in a fixed order.
-        double o = (in && i != j) ? a[i][j] * a[i][j] : 0.0;
+        double o = (in && i != j) ? a[cur][i][j] * a[cur][i][j] : 0.0;
         for (int m = 32; m >= 1; m >>= 1) o += __shfl_xor(o, m);
         if ((tid & 63) == 0) wsum[tid >> 6] = o;
         __syncthreads();
@@ -205,14 +209,15 @@ __global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, i
         // largest eigenvalues (cyclic Jacobi converges quadratically).
         if (!(tot > 1e-28 * scale * scale)) break;
         for (int round = 0; round < n - 1; ++round) {
+            const double (*ac)[kFMaxL + 1] = a[cur];
             if (tid < n / 2) {
                 int p, q;
                 if (tid == 0) { p = n - 1; q = round % (n - 1); }
                 else { p = (round + tid) % (n - 1); q = (round + n - 1 - tid) % (n - 1); }
                 if (p > q) { const int t = p; p = q; q = t; }
                 double c = 1.0, sn = 0.0;
-                if (q < l && a[p][q] != 0.0) {
-                    const double th = (a[q][q] - a[p][p]) / (2.0 * a[p][q]);
+                if (q < l && ac[p][q] != 0.0) {
+                    const double th = (ac[q][q] - ac[p][p]) / (2.0 * ac[p][q]);
                     const double t = (th >= 0.0 ? 1.0 : -1.0) / (__builtin_fabs(th) + __builtin_sqrt(th * th + 1.0));
                     c = 1.0 / __builtin_sqrt(t * t + 1.0);
                     sn = t * c;
@@ -222,34 +227,33 @@ __global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, i
                 if (q < l) { ptn[q] = p; rc[q] = c; rs_[q] = sn; }
             }
             __syncthreads();
-            double na = 0.0, nv = 0.0;
             if (in) {
                 const int pi = ptn[i], pj = ptn[j];
                 const double ci = rc[i], si = rs_[i], cj = rc[j], sj = rs_[j];
-                na = ci * (cj * a[i][j] + sj * a[i][pj]) + si * (cj * a[pi][j] + sj * a[pi][pj]);
-                nv = cj * v[i][j] + sj * v[i][pj];
+                a[cur ^ 1][i][j] = ci * (cj * ac[i][j] + sj * ac[i][pj]) + si * (cj * ac[pi][j] + sj * ac[pi][pj]);
+                v[cur ^ 1][i][j] = cj * v[cur][i][j] + sj * v[cur][i][pj];
             }
             __syncthreads();
-            if (in) { a[i][j] = na; v[i][j] = nv; }
-            __syncthreads();
+            cur ^= 1;
         }
     }
     // Sort by eigenvalue, descending (ties keep index order).
+    const double (*af)[kFMaxL + 1] = a[cur];
     if (tid == 0) {
         for (int k = 0; k < l; ++k) order[k] = k;
         for (int k = 0; k < l; ++k) {
             int best = k;
             for (int m = k + 1; m < l; ++m)
-                if (a[order[m]][order[m]] > a[order[best]][order[best]]) best = m;
+                if (af[order[m]][order[m]] > af[order[best]][order[best]]) best = m;
             const int t = order[k]; order[k] = order[best]; order[best] = t;
         }
     }
     __syncthreads();
     if (tid < l) {
-        const double ev = a[order[tid]][order[tid]];
+        const double ev = af[order[tid]][order[tid]];
         sig[tid] = __builtin_sqrt(ev > 0.0 ? ev : 0.0);
     }
-    if (in) U[i * l + j] = v[i][order[j]];
+    if (in) U[i * l + j] = v[cur][i][order[j]];
 }
 
 static unsigned jacobi_threads(int l) { return (unsigned)((l * l + 63) / 64 * 64); }
