@@ -368,6 +368,25 @@ def test_output_error_within_half_step_bound():
     assert np.all(np.abs(out["Y"] - exact) <= bound * (1 + 1e-9))
 
 
+def test_loss_hand_values():
+    # [TTQ §method b3] L = sum over tokens of ||(W - W_hat) x_t||^2.  One
+    # perturbed weight W[1][2] -> W[1][2] - 0.5 and two tokens whose channel
+    # 2 holds 5 and 7: output row 1 changes by 0.5 * 5 and 0.5 * 7, so
+    # L = 0.25 * (25 + 49) = 18.5 exactly.  T (2) differs from K (4) and M
+    # (3), so a transposed operand cannot give the same value.
+    X = np.array([[1.0, -2.0, 5.0, 0.5], [3.0, 1.0, 7.0, -4.0]], dtype=np.float32)
+    W = np.arange(12, dtype=np.float32).reshape(3, 4) / 8
+    w_eff = W.astype(np.float64).copy()
+    w_eff[1, 2] -= 0.5
+    assert oracle.loss(X, "f32", W, "f32", w_eff) == 18.5
+    # a perturbation in a channel both tokens leave at zero costs nothing
+    X0 = X.copy()
+    X0[:, 3] = 0.0
+    w3 = W.astype(np.float64).copy()
+    w3[0, 3] += 1.0
+    assert oracle.loss(X0, "f32", W, "f32", w3) == 0.0
+
+
 def test_activation_aware_loss_not_above_rtn_on_outlier_inputs():
     # [TTQ §method b3] objective L = ||(W - W_hat) X||^2; with outlier
     # channels the AWQ-scaled quantization must not lose to plain RTN.
