@@ -24,6 +24,20 @@ def _bf16(a):
 
 # ----------------------------------------------------------------- stats
 
+def test_decode_bf16_bit_patterns():
+    # bf16 is the upper half of an IEEE binary32: 0x3F80 = 1.0, 0xC000 = -2.0,
+    # 0x3EAB = 0.333984375 (the bf16 nearest 1/3), 0x0001 = 2^-133 (the
+    # smallest subnormal), 0x7F80 = +inf, 0x8000 = -0.0.
+    bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0001, 0x7F80, 0x8000], dtype=np.uint16)
+    got = oracle.decode(bits, "bf16")
+    assert got.dtype == np.float64
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 0.333984375
+    assert got[3] == 2.0 ** -133 and np.isposinf(got[4])
+    assert got[5] == 0.0 and np.signbit(got[5])
+    f = np.array([1.5, -0.1], dtype=np.float32)
+    assert np.array_equal(oracle.decode(f, "f32"), f.astype(np.float64))
+
+
 def test_stats_closed_form_plus_minus_a():
     # [TTQ §method b2-b3]: channel j holding +-a_j in every token has
     # second moment a_j^2, so ssq_j = T a_j^2 exactly (dyadic a_j).
