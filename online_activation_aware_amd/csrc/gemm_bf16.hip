@@ -36,7 +36,7 @@ template <int BN, bool YF32, bool LR>
 __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const uint16_t* __restrict__ Wq,
     int64_t ldw, int64_t M, void* __restrict__ Y, int64_t ldy, int yvec, const float* __restrict__ Z,
-    const float* __restrict__ Bm, int rank, int64_t zstride) {
+    const float* __restrict__ Bm, int rank, int nz, int64_t zstride) {
     constexpr int NW = kBThreads / kWave;                       // 8 waves
     constexpr int WT = BN / 4;                                  // tokens per wave (64 or 32)
     constexpr int FB = WT / 16;                                 // token fragments per wave
@@ -181,7 +181,12 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         float* bs = (float*)sW0;                  // [rank][128]
         for (int idx = tid; idx < rank * BN; idx += kBThreads) {
             const int k = idx / BN, tt = idx % BN;
-            zs[idx] = (t0 + tt < T) ? Z[(t0 + tt) * rank + k] : 0.0f;
+            float zv = 0.0f;
+            if (t0 + tt < T) {                    // Z's K-slice partials, added in slice order
+                zv = Z[(t0 + tt) * rank + k];
+                for (int p = 1; p < nz; ++p) zv += Z[((int64_t)p * T + t0 + tt) * rank + k];
+            }
+            zs[idx] = zv;
         }
         for (int idx = tid; idx < rank * kBM; idx += kBThreads) {
             const int k = idx / kBM, oo = idx % kBM;
@@ -265,6 +270,7 @@ hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
     const float* Z = lr ? lr->Z : nullptr;
     const float* B = lr ? lr->B : nullptr;
     const int rank = lr ? lr->rank : 0;
+    const int nz = lr ? lr->nz : 1;
     const int S = (lr == nullptr && split_ws != nullptr) ? gemm_bf16_splits(T, K, M) : 1;
     if (S > 1) {
         // fp32 partials of the K slices into the workspace (rows of ldp
@@ -273,7 +279,7 @@ hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
         const dim3 grid((unsigned)mt, (unsigned)((T + 255) / 256), (unsigned)S);
         hipError_t e = launch_kernel(k_gemm_bf16<256, true, false>, grid, dim3(kBThreads), 0, st, tm.start,
                                      nullptr, X, T, K / S, ldx, Wq, ldw, M, (void*)split_ws, ldp, 1,
-                                     (const float*)nullptr, (const float*)nullptr, 0, zs);
+                                     (const float*)nullptr, (const float*)nullptr, 0, 1, zs);
         if (e != hipSuccess) return e;
         const int64_t work = T * ((M + 3) / 4);
         const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 4096);
@@ -289,7 +295,7 @@ hipError_t launch_gemm_bf16(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
     const dim3 grid((unsigned)mt, (unsigned)((T + (narrow ? 127 : 255)) / (narrow ? 128 : 256)));
 #define TTQ_B_LAUNCH(BN, YF, LRF)                                                                          \
     return launch_kernel(k_gemm_bf16<BN, YF, LRF>, grid, dim3(kBThreads), 0, st, tm.start, tm.stop, X, T, K, \
-                         ldx, Wq, ldw, M, Y, ldy, yvec, Z, B, rank, (int64_t)0)
+                         ldx, Wq, ldw, M, Y, ldy, yvec, Z, B, rank, nz, (int64_t)0)
 #define TTQ_B_LAUNCH2(BN)                                 \
     if (rank > 0) {                                       \
         if (yf32) TTQ_B_LAUNCH(BN, true, true);           \

@@ -17,9 +17,10 @@ struct StageTimer {
 
 // Low-rank term added in the projection GEMM's epilogue: Y += Z B^T, fp32.
 struct LowrankEpilogue {
-    const float* Z;   // [T][rank]
+    const float* Z;   // [nz][T][rank]: Z = the nz partials added in order
     const float* B;   // [M][rank]
     int rank;
+    int nz = 1;
 };
 
 template <typename F, typename... Args>
@@ -109,8 +110,11 @@ hipError_t launch_qgemv(const void* X, bool xf32, int64_t T, int64_t K, int64_t 
 // Z = X A^T (fp32, [T][rank]) on the matrix cores, for bf16 X, K % 32 == 0
 // and a 16-byte-aligned A.
 bool lowrank_z_mfma_ok(bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A);
+// parts > 1: K is cut into `parts` slices and Z holds their partials
+// [parts][T][rank] (lowrank_zm_parts(T, K) fills the chip).
 hipError_t launch_lowrank_z(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A,
-                            int rank, float* Z, hipStream_t st, StageTimer tm = {});
+                            int rank, float* Z, hipStream_t st, StageTimer tm = {}, int parts = 1);
+int lowrank_zm_parts(int64_t T, int64_t K);
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                           int64_t ldy, float* Zp, hipStream_t st, StageTimer tm = {});

@@ -6,8 +6,10 @@
 // k_lowrank_zm (bf16 X, K % 32 == 0): Z on the matrix cores.  A (fp32) is
 // split into three bf16 terms hi + mid + lo (the remainder is below 2^-24 of
 // A), X is bf16 already and the MFMA accumulates in fp32, so Z keeps fp32
-// accuracy.  A workgroup owns 16 tokens; its 16 waves take the 32-wide K steps
-// w, w + 16, ... and their tiles are added in wave order.
+// accuracy.  A workgroup owns 16 tokens and one K slice (grid.y; one slice
+// unless the token tiles alone leave most compute units idle); its 16 waves
+// take the slice's 32-wide K steps w, w + 16, ... and their tiles are added in
+// wave order.  Slice y writes its partial Z to Z + y T rank.
 // k_lowrank_z (fp32 X or other K): one wave per 64 tokens and K slice (lane =
 // token); A's values are the same for every lane, so they come through scalar
 // loads, and each lane accumulates rank partial sums of its token over the
@@ -41,9 +43,13 @@ __global__ __launch_bounds__(kZWaves * kWave) void k_lowrank_zm(const uint16_t* 
     f32x4 acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int64_t nsteps = K / 32;
+    const int64_t nsall = K / 32;
+    const int64_t spp = (nsall + gridDim.y - 1) / gridDim.y;       // steps per slice
+    const int64_t sbeg = (int64_t)blockIdx.y * spp;
+    const int64_t nsteps = min(nsall, sbeg + spp);                  // end of this slice
+    Z += (int64_t)blockIdx.y * T * rank;
     constexpr int U = 4;                          // steps whose loads are in flight together
-    for (int64_t sb = wave; sb < nsteps; sb += (int64_t)U * kZWaves) {
+    for (int64_t sb = sbeg + wave; sb < nsteps; sb += (int64_t)U * kZWaves) {
         u32x4 xb[U];
         f32x4 a0[U][RT], a1[U][RT];
 #pragma unroll
@@ -113,10 +119,22 @@ bool lowrank_z_mfma_ok(bool xf32, int64_t T, int64_t K, int64_t ldx, const float
            (uintptr_t)A % 16 == 0;
 }
 
+// K slices for Z when its 16-token tiles leave most of the 256 compute units
+// idle (2048 tokens: 128 tiles, 2 slices), each slice at least one step per
+// wave; at most 8.
+int lowrank_zm_parts(int64_t T, int64_t K) {
+    const int64_t tiles = (T + 15) / 16;
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t smax = (K / 32) / kZWaves;
+    if (s > 8) s = 8;
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : (int)s;
+}
+
 hipError_t launch_lowrank_z(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* A,
-                            int rank, float* Z, hipStream_t st, StageTimer tm) {
-    if (!lowrank_z_mfma_ok(xf32, T, K, ldx, A)) return hipErrorInvalidValue;
-    const dim3 g((unsigned)((T + 15) / 16));
+                            int rank, float* Z, hipStream_t st, StageTimer tm, int parts) {
+    if (!lowrank_z_mfma_ok(xf32, T, K, ldx, A) || parts < 1) return hipErrorInvalidValue;
+    const dim3 g((unsigned)((T + 15) / 16), (unsigned)parts);
     if (rank <= 16)
         return launch_kernel(k_lowrank_zm<1>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop,
                              (const uint16_t*)X, T, K, ldx, A, rank, Z);
@@ -230,7 +248,8 @@ static hipError_t launch_lr(const void* X, bool xf32, int64_t T, int64_t K, int6
                             int64_t ldy, float* Zp, hipStream_t st, StageTimer tm) {
     int ns = 1;
     if (lowrank_z_mfma_ok(xf32, T, K, ldx, A)) {
-        if (hipError_t e = launch_lowrank_z(X, xf32, T, K, ldx, A, rank, Zp, st, {tm.start, nullptr})) return e;
+        ns = lowrank_zm_parts(T, K);
+        if (hipError_t e = launch_lowrank_z(X, xf32, T, K, ldx, A, rank, Zp, st, {tm.start, nullptr}, ns)) return e;
     } else {
         int64_t len = 0;
         ns = lowrank_slices(T, K, &len);

@@ -130,7 +130,8 @@ bool use_dequant_gemm(int64_t T, bool xf32, int64_t K, int64_t ldx) {
 size_t ws_lowrank(int64_t T, int64_t K, int rank) {
     if (rank <= 0 || T <= 0) return 0;
     int64_t len = 0;
-    const int ns = ttq::lowrank_slices(T, K, &len);
+    int ns = ttq::lowrank_slices(T, K, &len);
+    if (ttq::lowrank_zm_parts(T, K) > ns) ns = ttq::lowrank_zm_parts(T, K);
     return round_up((size_t)ns * (size_t)T * (size_t)rank * sizeof(float));
 }
 
@@ -150,7 +151,8 @@ StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, i
     size_t scratch = ws_stats(T, K);
     // prompt-sized projections: the dequantized weight, then Z = X A^T for
     // the low-rank epilogue
-    const size_t proj = ws_qgemm(T, K, M) + (rank > 0 && T > 0 ? round_up((size_t)T * rank * sizeof(float)) : 0);
+    const size_t proj = ws_qgemm(T, K, M) + (rank > 0 && T > 0 ? round_up((size_t)ttq::lowrank_zm_parts(T, K) *
+                                                                          T * rank * sizeof(float)) : 0);
     if (proj > scratch) scratch = proj;
     if (ws_lowrank(T, K, rank) > scratch) scratch = ws_lowrank(T, K, rank);
     L.total = off + scratch;
@@ -433,9 +435,10 @@ static ttq_status linear_layer(const ttq_linear_args* a, const double* ssq, cons
         const bool fuse = a->rank > 0 && ttq::lowrank_z_mfma_ok(xf32, a->T, a->K, a->ldx, a->A);
         if (fuse) {
             float* Z = (float*)((char*)scratch + ws_qgemm(a->T, a->K, a->M));
-            if (ttq_status e = device_status(
-                    ttq::launch_lowrank_z(a->X, xf32, a->T, a->K, a->ldx, a->A, a->rank, Z, st, timer(3)),
-                    "lowrank Z"))
+            lre.nz = ttq::lowrank_zm_parts(a->T, a->K);
+            if (ttq_status e = device_status(ttq::launch_lowrank_z(a->X, xf32, a->T, a->K, a->ldx, a->A, a->rank, Z,
+                                                                   st, timer(3), lre.nz),
+                                             "lowrank Z"))
                 return e;
             lre.Z = Z;
         }
