@@ -357,14 +357,16 @@ def _offset_dev(a: np.ndarray) -> torch.Tensor:
     return buf[1:].view(a.shape)
 
 
-@pytest.mark.parametrize("xdt,rank,a_off", [("bf16", 16, False), ("f32", 7, False), ("bf16", 32, False),
-                                            ("bf16", 16, True), ("bf16", 5, False)])
-def test_lowrank_add_parity(T, xdt, rank, a_off):
+@pytest.mark.parametrize("xdt,rank,a_off,K", [("bf16", 16, False, 512), ("f32", 7, False, 512),
+                                              ("bf16", 32, False, 512), ("bf16", 16, True, 512),
+                                              ("bf16", 5, False, 512), ("bf16", 16, False, 4096)])
+def test_lowrank_add_parity(T, xdt, rank, a_off, K):
     # bf16 X with an aligned A runs Z on the matrix cores; fp32 X or an A
-    # that is not 16-byte aligned runs the K-slice kernel.
-    say(f"lowrank_add xdt={xdt} rank={rank} A offset={a_off}")
+    # that is not 16-byte aligned runs the K-slice kernel.  K = 4096 with 150
+    # tokens (10 token tiles) splits the matrix-core Z into 8 K slices.
+    say(f"lowrank_add xdt={xdt} rank={rank} A offset={a_off} K={K}")
     rng = np.random.default_rng(rank)
-    Tn, K, M = 150, 512, 200
+    Tn, M = 150, 200
     X = synth.encode(rng.standard_normal((Tn, K)), xdt)
     A = (rng.standard_normal((rank, K)) * 0.05).astype(np.float32)
     B = (rng.standard_normal((M, rank))).astype(np.float32)
@@ -392,6 +394,8 @@ E2E = [
     ("c3-long", dict(T=400, K=1024, M=320)),
     ("c4-long", dict(T=256, K=2048, M=256)),
     ("c5-long", dict(T=260, K=512, M=512)),
+    # low-rank Z split into 4 K slices, summed in the GEMM epilogue
+    ("c5-slices", dict(T=300, K=2048, M=256)),
     # few 128 x 256 tiles and K >= 8192: two K slices plus their ordered sum
     ("c4-split", dict(T=260, K=8192, M=302)),
 ]
