@@ -62,11 +62,12 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
     const int wave = tid / kWave;
     const int wm = wave >> 2, wn = wave & 3;      // 2 x 4 waves of 64 x WT
     // Tile order for the eight XCDs, each with its own L2: workgroups are
-    // dispatched to XCDs round-robin by linear id, so the ids an XCD receives
-    // are mapped to one compact block of 8 row tiles x (token tiles / 2)
-    // instead of every token tile (on the 4096 x 2048 output of a 4096-channel layer each XCD reads
-    // 16.8 MB of operands instead of 21).  Grids that do not divide keep
-    // the plain order.
+    // dispatched to XCDs round-robin by linear id, so the n/8 ids an XCD
+    // receives are given consecutive places in an order that walks groups of
+    // 8 row tiles across the token tiles; each XCD then covers a compact
+    // block of the output (4096 x 2048 output: 8 row x 4 token tiles per XCD,
+    // 16.8 MB of operands read instead of 21).  Grids that do not divide
+    // keep the plain order.
     int64_t ob = blockIdx.x, tb = blockIdx.y;
     {
         const unsigned mt = gridDim.x, nt = gridDim.y, n = mt * nt;
