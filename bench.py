@@ -147,6 +147,24 @@ def cpu_baseline(wl, data, B=None, A=None) -> dict:
         stages["projection"].append(t3 - t2)
         assert np.isfinite(Y).all()
     dt = float(np.median(times))
+    # The same layer once more on one thread (BLAS limited to 1), when that
+    # stays within ~15 s of CPU time.
+    one_thread = None
+    if dt * threads <= 15.0:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                ssq = oracle.stats(data["X"], wl.xdtype)
+                s = oracle.awq_scales(ssq, wl.T, wl.alpha, wl.lambda_rel)
+                v = oracle.quant_values(data["W"], wl.wdtype, s, B, A)
+                r = oracle.group_rtn(v, wl.bits, wl.group)
+                oracle.pack_codes(r["q"], wl.bits)
+                w_hat = oracle.dequant(r["q"], r["delta"], r["zero"], wl.group)
+                oracle.project(data["X"], wl.xdtype, s, w_hat, B, A)
+                one_thread = round((time.perf_counter() - t0) * 1e6, 1)
+        except Exception:  # pragma: no cover
+            one_thread = None
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -162,6 +180,7 @@ def cpu_baseline(wl, data, B=None, A=None) -> dict:
                       f"quantize, pack, dequantize, projection), median of {len(times)} runs "
                       f"({sum(times):.1f} s of CPU work); cores = BLAS threads",
             "stages_us": {k: round(float(np.median(v)) * 1e6, 1) for k, v in stages.items()},
+            "one_thread_us": one_thread,
             "cpu_model": cpu_model, "host_cpus": avail}
 
 
