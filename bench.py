@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the TTQ per-prompt layer path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|c1..c5]
 
 A step is one pass of the whole per-prompt path for one linear layer —
 activation statistics -> shrunk AWQ scales -> group RTN of the scaled weight
@@ -9,6 +9,12 @@ activation statistics -> shrunk AWQ scales -> group RTN of the scaled weight
 through the C ABI's ttq_linear, on synthetic inputs already resident in HBM.
 Inputs rotate over several copies (>= 768 MiB in total) so that successive
 steps do not find X and W in the 256 MiB Infinity Cache.
+
+By default the 4096->4096, T = 2048 layer is the headline (the JSON line's
+value, roofline and CPU baseline), and the other four workloads (768->768
+fp32; 4096->14336; 14336->4096 with its decode steps and batched decode;
+the low-rank 4096->4096 layer with its per-prompt factors) are timed in the
+same run under "workloads".
 
 Prints one JSON line (stdout): the layer time in microseconds, the roofline
 of the dominant kernel (the projection GEMM) from HIP events that ttq_linear
@@ -184,47 +190,38 @@ def cpu_baseline(wl, data, B=None, A=None) -> dict:
             "cpu_model": cpu_model, "host_cpus": avail}
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # 200 warm-up steps (20-40 ms of work): after a shorter warm-up the GPU's
-    # clocks are still rising and the first timed steps run ~10% slower.
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: 4096->4096, T=2048)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--min-rotation-mib", type=int, default=768)
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="only run a plain device copy of this size (for HBM counter scaling)")
-    args = ap.parse_args(argv)
+def _graph_time_us(calls, reps: int, warm: int) -> float:
+    """Average µs of one call of ``calls`` (a Python function enqueuing a list
+    of n calls), captured once in a HIP graph and replayed ``reps`` times."""
+    import torch
+    calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        n = calls()
+    torch.cuda.synchronize()
+    for _ in range(max(1, warm)):
+        graph.replay()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record()
+    for _ in range(reps):
+        graph.replay()
+    f1.record()
+    torch.cuda.synchronize()
+    return f0.elapsed_time(f1) / (reps * n) * 1e3
 
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the path needs no cross-GPU exchange and each GPU runs it independently.", file=sys.stderr)
-        return 2
 
+def bench_workload(wl, args, dev, with_cpu: bool) -> dict:
+    """Time one workload: the whole layer (timed region), its stages (kernel
+    stamps), and, where the workload has them, decode steps and per-prompt
+    factors.  Returns a dict of results (µs, rates, fractions of peak)."""
     import numpy as np
     import torch
     from online_activation_aware_amd import synth, ttq
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        return 1
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"copied {n} bytes 3 times")
-        return 0
-
-    ttq.lib()  # fail loudly if the HIP library is missing
-    wl = synth.workload(args.workload)
     log(f"workload {wl.key}: {wl.name}")
     data = synth.make_inputs(wl)
 
@@ -271,8 +268,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # Timed region (`value`): K steps back to back, each ttq_linear called
-    # from Python, nothing else on the stream.
+    # Timed region: K steps back to back, each ttq_linear called from
+    # Python, nothing else on the stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -289,7 +286,8 @@ def main(argv=None) -> int:
     # with its own kernels' start and end times on the launch stream
     # (hipExtLaunchKernel), one (start, stop) pair per stage.  The stamps cost
     # a few microseconds of launch latency per kernel, so this region is not
-    # the one `value` comes from; the kernel durations themselves are exact.
+    # the one the layer time comes from; the kernel durations themselves are
+    # exact.
     evs = [ttq.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -308,20 +306,6 @@ def main(argv=None) -> int:
     flops = 2.0 * wl.T * wl.M * wl.K
     proj_us = stage_ms["projection"] * 1e3
     achieved = flops / (proj_us * 1e-6) / 1e12
-    h = kernel_source_hash()
-    tr = MEASURED_TRAFFIC.get(h)
-    traffic = tr["fetch_bytes"] + tr["write_bytes"] if tr and tr["workload"] == wl.key else None
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "k_gemm_bf16 (Y = X W~^T on the dequantized weight; bf16 MFMA 16x16x32, "
-                          "fp32 accumulate, 128x256 tiles, buffer->LDS DMA)",
-                "flops_per_launch": flops, "avg_launch_us": round(proj_us, 2),
-                "traffic_detail": (None if traffic is None else
-                                   {"fetch_bytes": tr["fetch_bytes"], "write_bytes": tr["write_bytes"],
-                                    "operand_bytes": alg["projection"],
-                                    "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (1 GiB copy calibration)"}),
-                "timing": "kernel start/end stamped into HIP events by ttq_linear on its stream "
-                          f"(hipExtLaunchKernel), averaged over {args.steps} instrumented steps"}
     breakdown = {}
     for name, v in stage_ms.items():
         us = v * 1e3
@@ -332,10 +316,11 @@ def main(argv=None) -> int:
             d["alg_bytes"] = alg[name]
             d["gbs"] = round(alg[name] / (us * 1e-6) / 1e9, 1)
             d["hbm_frac"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
-        if name == "quantize":
+        if name == "quantize" and wl.T >= 192 and wl.xdtype == "bf16":
             d["staged_bytes"] = wl.M * wl.K * 2     # dequantized weight written for the projection
         breakdown[name] = d
     breakdown["projection"]["tflops"] = round(achieved, 2)
+    breakdown["projection"]["mfma_frac"] = round(achieved / PEAK_BF16_TFLOPS, 4)
     for name, d in breakdown.items():
         log(f"  {name:10s} {d['us']:8.2f} us" + (f"  {d['gbs']:8.1f} GB/s" if "gbs" in d else "")
             + (f"  {d['tflops']:8.1f} TFLOP/s" if "tflops" in d else ""))
@@ -359,31 +344,14 @@ def main(argv=None) -> int:
                 for q in states:
                     ttq.ttq_qgemm(Xd, q["s"], q["codes"], q["scale_f16"], q["zero_f16"], wl.M, wl.bits,
                                   wl.group, Y=Yd, ws=wsd)
-            dsteps()
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.graph(graph, stream=side):
-                dsteps()
-            torch.cuda.synchronize()
-            reps = max(1, math.ceil(args.steps / nst))
-            for _ in range(max(1, math.ceil(args.warmup / nst))):
-                graph.replay()
-            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            f0.record()
-            for _ in range(reps):
-                graph.replay()
-            f1.record()
-            torch.cuda.synchronize()
-            us = f0.elapsed_time(f1) / (reps * nst) * 1e3
+                return len(states)
+            us = _graph_time_us(dsteps, max(1, math.ceil(args.steps / nst)), math.ceil(args.warmup / nst))
             b = sbytes + wl.K * 4 + td * wl.K * esize(wl.xdtype) + td * wl.M * 4
             decode[str(td)] = {"us": round(us, 2), "alg_bytes": b, "gbs": round(b / (us * 1e-6) / 1e9, 1),
                                "hbm_frac": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                                "flops": 2 * td * wl.M * wl.K}
             log(f"  decode T={td:<3d} {us:8.2f} us  {decode[str(td)]['gbs']:8.1f} GB/s "
-                f"({nst} rotating state copies, graph of {nst} steps x {reps})")
+                f"({nst} rotating state copies in one graph)")
 
         # One decode token for each of P prompts (each with its own quantized
         # state) in one ttq_qgemm_batched launch, over rotating groups.
@@ -398,24 +366,8 @@ def main(argv=None) -> int:
             for g in groups:
                 ttq.ttq_qgemm_batched(Xb, g["s"], g["codes"], g["scale_f16"], g["zero_f16"], wl.M, wl.bits,
                                       wl.group, Y=Yb)
-        bsteps()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(graph, stream=side):
-            bsteps()
-        torch.cuda.synchronize()
-        reps = max(1, math.ceil(args.steps / ngr))
-        graph.replay()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        f0.record()
-        for _ in range(reps):
-            graph.replay()
-        f1.record()
-        torch.cuda.synchronize()
-        us = f0.elapsed_time(f1) / (reps * ngr) * 1e3
+            return len(groups)
+        us = _graph_time_us(bsteps, max(1, math.ceil(args.steps / ngr)), 1)
         b = P * (sbytes + wl.K * 4 + wl.K * esize(wl.xdtype) + wl.M * 4)
         decode["batched_P8_T1"] = {"us": round(us, 2), "prompts": P, "alg_bytes": b,
                                    "gbs": round(b / (us * 1e-6) / 1e9, 1),
@@ -423,35 +375,119 @@ def main(argv=None) -> int:
                                    "tokens_per_s": round(P / (us * 1e-6), 1)}
         log(f"  decode P={P} prompts x T=1 {us:8.2f} us  {decode['batched_P8_T1']['gbs']:8.1f} GB/s "
             f"({ngr} rotating groups)")
+        del states, groups
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         log("timing the CPU oracle on the same layer ...")
         cpu = cpu_baseline(wl, data, B_h, A_h)
         log(f"  oracle: {cpu['value'] / 1e6:.2f} s/layer on {cpu['cores']} BLAS threads")
 
+    out = {"us_per_layer": round(ms * 1e3, 3), "workload": wl.name,
+           "config": {"workload": wl.name, "T": wl.T, "K": wl.K, "M": wl.M, "bits": wl.bits, "group": wl.group,
+                      "alpha": wl.alpha, "lambda_rel": wl.lambda_rel, "rank": wl.rank, "x_dtype": wl.xdtype,
+                      "w_dtype": wl.wdtype, "y_dtype": "f32",
+                      "cache": f"{ncopy} rotating copies of X and W ({ncopy * per_copy / 2**20:.0f} MiB)"},
+           "stages": breakdown, "decode": decode, "factors": factors, "cpu_baseline": cpu,
+           "projection_flops": flops, "projection_us": proj_us}
+    del Xs, Ws, X0, W0, st, ws, Y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    # 200 warm-up steps (20-40 ms of work): after a shorter warm-up the GPU's
+    # clocks are still rising and the first timed steps run ~10% slower.
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="all",
+                    help="all (default: c2 as the headline, then c1, c3, c4, c5) or one of c1..c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-mib", type=int, default=768)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (for HBM counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the path needs no cross-GPU exchange and each GPU runs it independently.", file=sys.stderr)
+        return 2
+
+    import torch
+    from online_activation_aware_amd import synth, ttq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return 0
+
+    ttq.lib()  # fail loudly if the HIP library is missing
+    keys = ["c2", "c1", "c3", "c4", "c5"] if args.workload == "all" else [args.workload]
+    results = {}
+    for i, key in enumerate(keys):
+        results[key] = bench_workload(synth.workload(key), args, dev, with_cpu=(i == 0 and not args.no_cpu_baseline))
+    head = results[keys[0]]
+
+    proj_us = head["projection_us"]
+    achieved = head["projection_flops"] / (proj_us * 1e-6) / 1e12
+    h = kernel_source_hash()
+    tr = MEASURED_TRAFFIC.get(h)
+    traffic = tr["fetch_bytes"] + tr["write_bytes"] if tr and tr["workload"] == keys[0] else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "k_gemm_bf16 (Y = X W~^T on the dequantized weight; bf16 MFMA 16x16x32, "
+                          "fp32 accumulate, buffer->LDS DMA)",
+                "flops_per_launch": head["projection_flops"], "avg_launch_us": round(proj_us, 2),
+                "traffic_detail": (None if traffic is None else
+                                   {"fetch_bytes": tr["fetch_bytes"], "write_bytes": tr["write_bytes"],
+                                    "source": "stored: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE taken on this "
+                                              "kernel source (hash " + h + "), not measured in this run",
+                                    "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (1 GiB copy calibration)"}),
+                "timing": "kernel start/end stamped into HIP events by ttq_linear on its stream "
+                          f"(hipExtLaunchKernel), averaged over {args.steps} instrumented steps"}
+
+    def summary(r):
+        d = {"us_per_layer": r["us_per_layer"], "config": r["config"], "stages": r["stages"]}
+        if r["decode"]:
+            d["decode"] = r["decode"]
+        if r["factors"]:
+            d["factors"] = r["factors"]
+        return d
+
     out = {
         "metric": METRIC,
-        "value": round(ms * 1e3, 3),
+        "value": head["us_per_layer"],
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": round(head["us_per_layer"] / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "K": wl.K, "M": wl.M, "bits": wl.bits, "group": wl.group,
-                   "alpha": wl.alpha, "lambda_rel": wl.lambda_rel, "rank": wl.rank, "x_dtype": wl.xdtype,
-                   "w_dtype": wl.wdtype, "y_dtype": "f32",
-                   "cache": f"{ncopy} rotating copies of X and W ({ncopy * per_copy / 2**20:.0f} MiB)"},
+        "config": head["config"],
         "roofline": roofline,
-        "cpu_baseline": cpu,
-        "stages": breakdown,
-        "decode": decode,
-        "factors": factors,
+        "cpu_baseline": head["cpu_baseline"],
+        "stages": head["stages"],
+        "decode": head["decode"],
+        "factors": head["factors"],
+        "workloads": {k: summary(r) for k, r in results.items()},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -14,10 +14,13 @@
  *    W is [M][K] row-major with row stride ldw (the Linear weight layout),
  *    Y is [T][M] row-major with row stride ldy.
  *  - Every pointer is DEVICE memory, allocated and owned by the caller; the
- *    library allocates nothing, keeps no global mutable state and never
- *    synchronises.  Every call only enqueues kernels on `stream` (a
- *    hipStream_t; NULL = the null stream) and returns; results are ready
- *    when the stream reaches that point.
+ *    library allocates nothing and never synchronises.  Every call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *    and returns; results are ready when the stream reaches that point.
+ *    Global state: the calling thread's last error text, and a per-device
+ *    memo of kernel residency queried from the runtime once (a property of
+ *    the code object: it never changes a result).  Calls are safe from any
+ *    thread and on any stream.
  *  - Packed codes: for each output row, the K codes form a little-endian bit
  *    stream (code j occupies stream bits [bits*j, bits*j + bits), least
  *    significant bit first; stream bit i is bit i%32 of int32 word i/32).
@@ -37,11 +40,13 @@
  *    aligned.
  *  - Limits: K a positive multiple of 32 (of 8 for ttq_stats), at most 2^18;
  *    T, M and row strides at most 2^30; bits in
- *    {2,3,4,5}; group in {16,32,64,128} dividing K; 0 <= rank <= 32.
+ *    {2,3,4,5}; group in {16,32,64,128} dividing K; 0 <= rank <= 64
+ *    (ttq_lowrank_factors: rank <= l <= 32).
  *    T == 0 or M == 0 is a valid empty call (nothing is launched, except
  *    that ttq_stats with accumulate == 0 still zeroes ssq).
- *  - Inputs are expected to be finite.  Non-finite inputs give unspecified
- *    (but memory-safe) outputs.
+ *  - Inputs are expected to be finite.  The quantizer gives a NaN weight
+ *    code 0 and leaves it out of its group's range; other non-finite inputs
+ *    give unspecified (but memory-safe) outputs.
  */
 #ifndef TTQ_H
 #define TTQ_H

@@ -18,7 +18,8 @@
 // Fragments are double-buffered in registers: the LDS reads of one 32-deep
 // half overlap the MFMAs of the other, and waves raise their issue priority
 // while they feed the matrix cores.
-// Optionally the epilogue adds the low-rank term Z B^T (fp32) before the store.
+// Optionally the epilogue adds the low-rank term Z B^T (fp32, rank <= 64)
+// before the store.
 #include <algorithm>
 
 #include "common.hpp"
@@ -176,35 +177,40 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         // [TTQ §method b5] low-rank term Y += B (A X) = Z B^T, in fp32, added
         // before the store.  Every DMA has landed and every wave has passed
         // the last barrier, so the ring slots are free: the tile's Z (BN
-        // tokens) and B (128 rows), rank <= 32, are staged there transposed
-        // (rank-major), so lanes read consecutive tokens / rows.
-        float* zs = (float*)sX0;                  // [rank][BN]
-        float* bs = (float*)sW0;                  // [rank][128]
-        for (int idx = tid; idx < rank * BN; idx += kBThreads) {
-            const int k = idx / BN, tt = idx % BN;
-            float zv = 0.0f;
-            if (t0 + tt < T) {                    // Z's K-slice partials, added in slice order
-                zv = Z[(t0 + tt) * rank + k];
-                for (int p = 1; p < nz; ++p) zv += Z[((int64_t)p * T + t0 + tt) * rank + k];
+        // tokens) and B (128 rows) are staged there transposed (rank-major,
+        // so lanes read consecutive tokens / rows), 32 ranks at a time (what
+        // one slot holds); the ranks are added in order.
+        float* zs = (float*)sX0;                  // [32][BN]
+        float* bs = (float*)sW0;                  // [32][128]
+        for (int kc = 0; kc < rank; kc += 32) {
+            const int nk = min(32, rank - kc);
+            if (kc > 0) __syncthreads();          // the previous chunk's reads are done
+            for (int idx = tid; idx < nk * BN; idx += kBThreads) {
+                const int k = kc + idx / BN, tt = idx % BN;
+                float zv = 0.0f;
+                if (t0 + tt < T) {                // Z's K-slice partials, added in slice order
+                    zv = Z[(t0 + tt) * rank + k];
+                    for (int p = 1; p < nz; ++p) zv += Z[((int64_t)p * T + t0 + tt) * rank + k];
+                }
+                zs[idx] = zv;
             }
-            zs[idx] = zv;
-        }
-        for (int idx = tid; idx < rank * kBM; idx += kBThreads) {
-            const int k = idx / kBM, oo = idx % kBM;
-            bs[idx] = (o0 + oo < M) ? Bm[(o0 + oo) * rank + k] : 0.0f;
-        }
-        __syncthreads();
-        for (int k = 0; k < rank; ++k) {
-            float zt[FB];
+            for (int idx = tid; idx < nk * kBM; idx += kBThreads) {
+                const int k = kc + idx / kBM, oo = idx % kBM;
+                bs[idx] = (o0 + oo < M) ? Bm[(o0 + oo) * rank + k] : 0.0f;
+            }
+            __syncthreads();
+            for (int k = 0; k < nk; ++k) {
+                float zt[FB];
 #pragma unroll
-            for (int j = 0; j < FB; ++j) zt[j] = zs[k * BN + wn * WT + 16 * j + (lane & 15)];
+                for (int j = 0; j < FB; ++j) zt[j] = zs[k * BN + wn * WT + 16 * j + (lane & 15)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 bo = *(const f32x4*)(bs + k * kBM + wm * 64 + 16 * i + 4 * (lane >> 4));
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 bo = *(const f32x4*)(bs + k * kBM + wm * 64 + 16 * i + 4 * (lane >> 4));
 #pragma unroll
-                for (int j = 0; j < FB; ++j)
+                    for (int j = 0; j < FB; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(bo[r], zt[j], acc[i][j][r]);
+                        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(bo[r], zt[j], acc[i][j][r]);
+                }
             }
         }
     }

@@ -23,7 +23,7 @@
 
 namespace ttq {
 
-constexpr int kMaxRank = 32;
+constexpr int kMaxRank = 64;
 
 constexpr int kZWaves = 16;
 
@@ -138,7 +138,11 @@ hipError_t launch_lowrank_z(const void* X, bool xf32, int64_t T, int64_t K, int6
     if (rank <= 16)
         return launch_kernel(k_lowrank_zm<1>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop,
                              (const uint16_t*)X, T, K, ldx, A, rank, Z);
-    return launch_kernel(k_lowrank_zm<2>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop, (const uint16_t*)X,
+    if (rank <= 32)
+        return launch_kernel(k_lowrank_zm<2>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop,
+                             (const uint16_t*)X, T, K, ldx, A, rank, Z);
+    if (rank > kMaxRank) return hipErrorInvalidValue;
+    return launch_kernel(k_lowrank_zm<4>, g, dim3(kZWaves * kWave), 0, st, tm.start, tm.stop, (const uint16_t*)X,
                          T, K, ldx, A, rank, Z);
 }
 
@@ -270,10 +274,11 @@ static hipError_t launch_lr(const void* X, bool xf32, int64_t T, int64_t K, int6
 hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx,
                           const float* A, const float* B, int64_t M, int rank, void* Y, bool yf32,
                           int64_t ldy, float* Zp, hipStream_t st, StageTimer tm) {
-    // The accumulators are sized by the smallest of 8/16/32 that holds rank.
+    // The accumulators are sized by the smallest of 8/16/32/64 that holds rank.
     if (rank <= 8) return launch_lr<8>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
     if (rank <= 16) return launch_lr<16>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
-    if (rank <= kMaxRank) return launch_lr<32>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
+    if (rank <= 32) return launch_lr<32>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
+    if (rank <= kMaxRank) return launch_lr<64>(X, xf32, T, K, ldx, A, B, M, rank, Y, yf32, ldy, Zp, st, tm);
     return hipErrorInvalidValue;
 }
 

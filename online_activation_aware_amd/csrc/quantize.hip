@@ -10,7 +10,8 @@
 // its min/max needs log2(g/8) DPP lane exchanges.  Four adjacent lanes hold
 // 32 codes = `bits` int32 words, assembled with quad broadcasts and written
 // by the first `bits` lanes of the quad.  With low-rank factors, the strip of A
-// (rank x 512 fp32) is staged once in LDS and reused for every row.
+// (up to 32 ranks x 512 fp32) is staged once in LDS and reused for every row;
+// ranks 32..63 are read from global memory.
 //
 // Optionally the kernel also writes the dequantized weight of [TTQ §method b1]
 // (QDQ) with the input scale folded back, w~ = bf16(((code - zero) * step) *
@@ -27,6 +28,14 @@ namespace ttq {
 
 constexpr int kQThreads = 256;
 constexpr int kQChans = kWave * 8;
+constexpr int kQLdsRanks = 32;       // ranks of A staged in LDS (64 KB)
+
+// Workgroups of one quantizer kernel resident at once, per device and per
+// number of A ranks staged in LDS (0 = not yet queried).
+constexpr int kMaxDevices = 64;
+struct OccMemo {
+    std::atomic<int> resident[kMaxDevices][kQLdsRanks + 1];
+};
 
 // Cross-lane moves through DPP (they run in the VALU pipeline, no LDS round
 // trip).  Quad permutations: lane i of each quad reads lane perm[i]
@@ -195,7 +204,9 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     const float* __restrict__ B, const float* __restrict__ A, int rank, int rows_per_block,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero,
     uint16_t* __restrict__ wq, QScaleSrc qs) {
-    extern __shared__ __attribute__((aligned(16))) float sA[];   // [rank][kQChans] when LOWRANK (16-B reads)
+    // [min(rank, kQLdsRanks)][kQChans] when LOWRANK (16-byte reads); ranks
+    // beyond kQLdsRanks are read from A in global memory (L2-resident).
+    extern __shared__ __attribute__((aligned(16))) float sA[];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // row addressing stays scalar
@@ -225,8 +236,9 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
             }
         }
     };
+    const int lds_ranks = rank < kQLdsRanks ? rank : kQLdsRanks;
     if constexpr (LOWRANK) {
-        for (int idx = threadIdx.x; idx < rank * kQChans; idx += kQThreads) {
+        for (int idx = threadIdx.x; idx < lds_ranks * kQChans; idx += kQThreads) {
             const int k = idx / kQChans, c = idx % kQChans;
             sA[idx] = (cbase + c < K) ? A[(int64_t)k * K + cbase + c] : 0.0f;
         }
@@ -296,13 +308,18 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
                 Brow[r] = B + (o < M ? o : M - 1) * rank;
             }
             for (int k = 0; k < rank; ++k) {
-                const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
-                const f32x4 a0 = ak[0], a1 = ak[1];
                 double ad[8];
+                if (k < lds_ranks) {
+                    const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
+                    const f32x4 a0 = ak[0], a1 = ak[1];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ad[i] = (double)a0[i];
-                    ad[4 + i] = (double)a1[i];
+                    for (int i = 0; i < 4; ++i) {
+                        ad[i] = (double)a0[i];
+                        ad[4 + i] = (double)a1[i];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ad[i] = active ? (double)A[(int64_t)k * K + col + i] : 0.0;
                 }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
@@ -355,31 +372,38 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
     const int rows = (lr || wf32 || rb4) ? 16 : 32;
     const int64_t strips = (K + kQChans - 1) / kQChans;
     const int64_t nrb = (M + rows - 1) / rows;
-    const size_t lds = lr ? (size_t)rank * kQChans * sizeof(float) : 0;
+    const size_t lds = lr ? (size_t)(rank < kQLdsRanks ? rank : kQLdsRanks) * kQChans * sizeof(float) : 0;
     const QScaleSrc q = qs ? *qs : QScaleSrc{};
-    // Persistent row loop: as many workgroups as the device holds at once
-    // (workgroups per compute unit cached per kernel and LDS size).
-    auto grid_for = [&](const void* kern, std::atomic<int>& cache) -> dim3 {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess)
-            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        int per_cu = lr ? 0 : cache.load(std::memory_order_relaxed);
-        if (per_cu < 1) {
+    // Persistent row loop: as many workgroups as the device holds at once.
+    // The residency of each kernel instantiation is memoized per device and
+    // per LDS size (0..32 staged ranks of A): a value the runtime derives
+    // from the code object, the same on every call, so the memo never
+    // changes a result.
+    const int lds_ranks = lr ? (rank < kQLdsRanks ? rank : kQLdsRanks) : 0;
+    auto grid_for = [&](const void* kern, OccMemo& memo) -> dim3 {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+        std::atomic<int>* slot = (dev >= 0 && dev < kMaxDevices) ? &memo.resident[dev][lds_ranks] : nullptr;
+        int resident = slot ? slot->load(std::memory_order_relaxed) : 0;
+        if (resident < 1) {
+            int cus = 256, per_cu = 1;
+            if (dev >= 0) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kQThreads, lds) != hipSuccess ||
                 per_cu < 1)
                 per_cu = 1;
-            if (!lr) cache.store(per_cu, std::memory_order_relaxed);
+            resident = cus * per_cu;
+            if (slot) slot->store(resident, std::memory_order_relaxed);
         }
-        int64_t gy = ((int64_t)cus * per_cu + strips - 1) / strips;
+        int64_t gy = ((int64_t)resident + strips - 1) / strips;
         if (gy > nrb) gy = nrb;
         if (gy > 65535) gy = 65535;
         return dim3((unsigned)strips, (unsigned)gy);
     };
 #define TTQ_Q_LAUNCH(WF, LR, SF, R4)                                                                     \
     do {                                                                                                 \
-        static std::atomic<int> occ{0};                                                                  \
+        static OccMemo memo;                                                                             \
         auto kern = k_quantize<BITS, GROUP, WF, LR, SF, R4>;                                             \
-        return launch_kernel(kern, grid_for((const void*)kern, occ), dim3(kQThreads), lds, st, tm.start,  \
+        return launch_kernel(kern, grid_for((const void*)kern, memo), dim3(kQThreads), lds, st, tm.start, \
                              tm.stop, W, M, K, ldw, s, B, A, rank, rows, codes, scale, zero, wq, q);     \
     } while (0)
 #define TTQ_Q_LAUNCH2(WF, LR, R4) \

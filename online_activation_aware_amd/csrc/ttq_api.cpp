@@ -1,8 +1,9 @@
 // The libttq C ABI: argument validation, workspace layout, launches.
 //
 // Every check runs on the host before any HIP call; a failed check returns
-// TTQ_ERR_INVALID / TTQ_ERR_UNSUPPORTED and launches nothing.  The library
-// keeps no global mutable state other than the per-thread error text.
+// TTQ_ERR_INVALID / TTQ_ERR_UNSUPPORTED and launches nothing.  Global state:
+// the per-thread error text, and a per-device memo of the quantizer's
+// residency (a property of the code object, so it never changes a result).
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -36,7 +37,7 @@ ttq_status device_status(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxK = (int64_t)1 << 18;    // input channels (block sums of the mean fit in LDS)
-constexpr int kMaxRank = 32;
+constexpr int kMaxRank = 64;
 constexpr size_t kAlign = 256;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

@@ -8,6 +8,8 @@ call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from typing import Optional
 
@@ -119,6 +121,33 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _torch_stream(stream) -> torch.cuda.Stream:
+    """The launch stream as a torch stream (a raw hipStream_t handle is
+    wrapped as an external stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _on_launch_stream(fn):
+    """Run a call with its launch stream as torch's current stream, so that
+    every tensor the binding allocates for it (outputs, default workspaces)
+    belongs to the stream the kernels run on: the caching allocator then
+    cannot hand such memory to other work before those kernels are done."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        bound = sig.bind(*args, **kwargs)
+        ts = _torch_stream(bound.arguments.get("stream"))
+        bound.arguments["stream"] = ts
+        with torch.cuda.stream(ts):
+            return fn(*bound.args, **bound.kwargs)
+    return call
+
+
 def _check(status: int) -> None:
     if status != TTQ_OK:
         L = lib()
@@ -147,6 +176,7 @@ def workspace(T: int, K: int, M: int, bits: int, group: int, rank: int = 0, devi
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+@_on_launch_stream
 def ttq_stats(X: torch.Tensor, ssq: torch.Tensor, accumulate: bool = False,
               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     if ssq.dtype != torch.float64:
@@ -158,6 +188,7 @@ def ttq_stats(X: torch.Tensor, ssq: torch.Tensor, accumulate: bool = False,
     return ssq
 
 
+@_on_launch_stream
 def ttq_stats_p(X: torch.Tensor, p: float, msum: torch.Tensor, accumulate: bool = False,
                 ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     if msum.dtype != torch.float64:
@@ -169,6 +200,7 @@ def ttq_stats_p(X: torch.Tensor, p: float, msum: torch.Tensor, accumulate: bool 
     return msum
 
 
+@_on_launch_stream
 def ttq_awq_scales(ssq: torch.Tensor, n_tokens: int, alpha: float, lambda_rel: float,
                    p: float = 2.0, s: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     K = ssq.numel()
@@ -179,6 +211,7 @@ def ttq_awq_scales(ssq: torch.Tensor, n_tokens: int, alpha: float, lambda_rel: f
     return s
 
 
+@_on_launch_stream
 def ttq_quantize_groups(W: torch.Tensor, s: Optional[torch.Tensor], bits: int, group: int,
                         B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
                         codes: Optional[torch.Tensor] = None, scale_f16: Optional[torch.Tensor] = None,
@@ -199,6 +232,7 @@ def ttq_quantize_groups(W: torch.Tensor, s: Optional[torch.Tensor], bits: int, g
     return codes, scale_f16, zero_f16
 
 
+@_on_launch_stream
 def ttq_qgemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: torch.Tensor,
               zero_f16: torch.Tensor, M: int, bits: int, group: int, Y: Optional[torch.Tensor] = None,
               y_dtype=torch.float32, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -213,6 +247,7 @@ def ttq_qgemm(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: 
     return Y
 
 
+@_on_launch_stream
 def ttq_qgemm_batched(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, scale_f16: torch.Tensor,
                       zero_f16: torch.Tensor, M: int, bits: int, group: int, Y: Optional[torch.Tensor] = None,
                       y_dtype=torch.float32, stream=None) -> torch.Tensor:
@@ -236,6 +271,7 @@ def ttq_qgemm_batched(X: torch.Tensor, s: torch.Tensor, codes: torch.Tensor, sca
     return Y
 
 
+@_on_launch_stream
 def ttq_lowrank_add(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, Y: torch.Tensor,
                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     T, K = X.shape
@@ -247,6 +283,7 @@ def ttq_lowrank_add(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, Y: torch.
     return Y
 
 
+@_on_launch_stream
 def ttq_lowrank_factors(W: torch.Tensor, s: torch.Tensor, omega: torch.Tensor, rank: int, q: int,
                         B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
                         ws: Optional[torch.Tensor] = None, stream=None):
@@ -270,6 +307,7 @@ def ttq_lowrank_factors(W: torch.Tensor, s: torch.Tensor, omega: torch.Tensor, r
     return B, A
 
 
+@_on_launch_stream
 def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: float,
                lambda_rel: float, p: float = 2.0, B: Optional[torch.Tensor] = None,
                A: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
@@ -302,6 +340,7 @@ def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: f
     return Y
 
 
+@_on_launch_stream
 def ttq_linear_shared(X: torch.Tensor, layers: list, alpha: float, lambda_rel: float, p: float = 2.0,
                       ws: Optional[torch.Tensor] = None, stream=None) -> list:
     """Several layers on the same X with one statistics pass.  ``layers``:

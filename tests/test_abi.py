@@ -70,7 +70,7 @@ def test_workspace_bytes(L):
                 (10, 128, 10, 6, 32, 0),     # bits
                 (10, 128, 10, 4, 48, 0),     # group
                 (10, 96, 10, 4, 64, 0),      # group does not divide K
-                (10, 128, 10, 4, 32, 33),    # rank
+                (10, 128, 10, 4, 32, 65),    # rank
                 (-1, 128, 10, 4, 32, 0)]:
         assert ttq.ttq_workspace_bytes(*bad) == 0
 
@@ -126,7 +126,7 @@ def test_quantize_rejects(L):
     assert call(K=48, ldw=48, group=16) == 1           # K not a multiple of 32
     assert call(rank=4) == 1                           # rank without factors
     assert call(rank=0, B=FAKE, A=FAKE) == 1           # factors without rank
-    assert call(rank=40, B=FAKE, A=FAKE) == 1          # rank above the limit
+    assert call(rank=65, B=FAKE, A=FAKE) == 1          # rank above the limit
     assert call(codes=None) == 1
     assert call(s=FAKE + 4) == 1
     assert call(M=-1) == 1

@@ -3,21 +3,25 @@
 The layer runs through ttq_linear in the configuration bench.py times: fp32
 Y, the prompt state returned, one workspace.  The checks are:
 
-- the statistics and scales of all K channels;
-- the quantization of sampled output rows against the oracle's own, using
-  the same bars as tests/test_gpu_parity.py;
-- Y on those rows for every token;
-- Y on every output for sampled tokens, against the dense projection of the
-  library's own quantized state (which covers every output tile);
+- the statistics and scales of all K channels (scales bit-identical to the
+  oracle's in almost every channel);
+- the quantization of sampled output rows against the oracle's group RTN on
+  the library's own scales (steps and zeros exact, codes exact outside the
+  rounding band, at most 1e-4 of them inside it);
+- Y on those rows for every token against the oracle (relative Frobenius);
+- every element of Y against the fp64 projection of the library's own
+  quantized state, within the element-wise bound of the single bf16 rounding
+  of the dequantized weight (tests/gpu_util.py);
 - for the 14336->4096 workload, the decode steps (T = 1, 4, 16) on the prompt
-  state.
+  state, the same way.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import host, rel_fro, say, to_dev, f32_dev
+from gpu_util import (check_quant_state, check_scales, f32_dev, host, rel_fro, say, to_dev,
+                      y_elementwise_check)
 from online_activation_aware_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +29,6 @@ pytestmark = pytest.mark.gpu
 Y_TOL = 2e-3
 S_TOL = 1e-5
 N_ROWS = 64
-N_TOKENS = 24
 
 
 @pytest.fixture(scope="module")
@@ -71,17 +74,14 @@ def test_fullsize_linear(T, key):
     # statistics and scales: every channel
     np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
     s = host(st["s"])
-    np.testing.assert_allclose(s, ref["s"], rtol=S_TOL)
+    check_scales(s, ref["s"], rtol=S_TOL)
     say(f"  scales identical: {np.array_equal(s, ref['s'])}")
 
-    # quantization of the sampled rows
-    codes, delta, zero = host(st["codes"])[rows], host(st["scale_f16"])[rows], host(st["zero_f16"])[rows]
-    if np.array_equal(s, ref["s"]):
-        np.testing.assert_array_equal(delta.view(np.float16), ref["delta"])
-        np.testing.assert_array_equal(zero.view(np.float16), ref["zero"])
-        gq = oracle.unpack_codes(codes, wl.bits, wl.K)
-        bad = (gq != ref["q"]) & ~oracle.boundary_band(ref["u"])
-        assert not bad.any(), f"{int(bad.sum())} codes differ outside the rounding band"
+    # quantization of the sampled rows, against the oracle on the library's s
+    codes_all, delta_all, zero_all = host(st["codes"]), host(st["scale_f16"]), host(st["zero_f16"])
+    nb = check_quant_state(codes_all[rows], delta_all[rows], zero_all[rows], np.asarray(d["W"])[rows],
+                           wl.wdtype, s, wl.bits, wl.group, None if B is None else B[rows], A)
+    say(f"  quantizer: {nb} in-band code differences on {len(rows)} rows")
 
     # Y on the sampled rows, every token, against the oracle's own quantization
     Yh = host(Y)
@@ -89,18 +89,11 @@ def test_fullsize_linear(T, key):
     say(f"  Y rel err (sampled rows, all tokens) {err:.3e}")
     assert err < Y_TOL
 
-    # Y on every output for sampled tokens, against the library's own state
-    toks = _sample(wl.T, N_TOKENS, 12, must=(0, wl.T - 1))
-    gq_all = oracle.unpack_codes(host(st["codes"]), wl.bits, wl.K)
-    w_hat = oracle.dequant(gq_all, host(st["scale_f16"]).view(np.float16),
-                           host(st["zero_f16"]).view(np.float16), wl.group)
-    Xs = np.asarray(d["X"])[toks]
-    ref_all = oracle.project(Xs, wl.xdtype, s, w_hat, B, A)
-    err_all = rel_fro(Yh[toks], ref_all)
-    say(f"  Y rel err (all outputs, sampled tokens) {err_all:.3e}")
-    assert err_all < Y_TOL
-    col_err = np.linalg.norm(Yh[toks] - ref_all, axis=0) / np.maximum(np.linalg.norm(ref_all, axis=0), 1e-30)
-    assert np.all(col_err < 2e-2), f"worst output column {int(np.argmax(col_err))}: {col_err.max():.3e}"
+    # every element of Y against the fp64 projection of the library's state
+    q_all = oracle.unpack_codes(codes_all, wl.bits, wl.K)
+    d16, z16 = delta_all.view(np.float16), zero_all.view(np.float16)
+    worst = y_elementwise_check(Yh, d["X"], wl.xdtype, s, q_all, d16, z16, wl.group, B, A)
+    say(f"  Y element-wise: worst |error| / bound {worst:.3f}")
 
     if wl.decode_T:
         ws = T.workspace(max(wl.decode_T), wl.K, wl.M, wl.bits, wl.group)
@@ -109,6 +102,7 @@ def test_fullsize_linear(T, key):
                              wl.M, wl.bits, wl.group, ws=ws)
             Ydh = host(Yd)
             e1 = rel_fro(Ydh[:, rows], oracle.project(Xd, wl.xdtype, ref["s"], ref["w_hat"]))
-            e2 = rel_fro(Ydh, oracle.project(Xd, wl.xdtype, s, w_hat))
-            say(f"  decode T={td}: rel err {e1:.3e} (oracle rows), {e2:.3e} (all outputs)")
-            assert e1 < Y_TOL and e2 < Y_TOL
+            wd = y_elementwise_check(Ydh, Xd, wl.xdtype, s, q_all, d16, z16, wl.group,
+                                     valu=(td <= 4 and wl.K % 128 == 0))
+            say(f"  decode T={td}: rel err {e1:.3e} (oracle rows), element-wise worst ratio {wd:.3f}")
+            assert e1 < Y_TOL

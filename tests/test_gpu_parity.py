@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bf16_bits_to_f64, f16_dev, f32_dev, host, i32_dev, rel_fro, say, to_dev
+from gpu_util import (bf16_bits_to_f64, check_codes, check_quant_state, check_scales, exact_ties, f16_dev, f32_dev,
+                      host, i32_dev, rel_fro, say, to_dev, y_elementwise_check)
 from online_activation_aware_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -34,14 +35,14 @@ def _inputs(key, seed=None, **sizes):
     return wl, synth.make_inputs(wl, seed=seed)
 
 
-def _check_codes(T, got_codes, or_q, or_u, bits, K):
-    gq = oracle.unpack_codes(got_codes, bits, K)
-    band = oracle.boundary_band(or_u)
-    bad = (gq != or_q) & ~band
-    assert not bad.any(), f"{int(bad.sum())} codes differ outside the rounding band"
-    # the GPU's words are a valid packing of its codes (layout round trip)
-    np.testing.assert_array_equal(oracle.pack_codes(gq, bits), got_codes)
-    return int(((gq != or_q) & band).sum())
+def _check_rtn(got_codes, got_delta, got_zero, v, bits, group):
+    """The library's codes, steps and zeros against the oracle's group RTN
+    of the values v."""
+    r = oracle.group_rtn(v, bits, group)
+    np.testing.assert_array_equal(host(got_delta), r["delta"])
+    np.testing.assert_array_equal(host(got_zero), r["zero"])
+    return check_codes(host(got_codes), r["q"], r["u"], bits, np.asarray(v).shape[1],
+                       exact_ties(v, r["delta"], group))
 
 
 # ------------------------------------------------------------------ stats
@@ -137,12 +138,8 @@ def test_quantize_parity(T, wdt, bits, group):
     rng = np.random.default_rng(bits * 1000 + group)
     W = synth.encode(rng.standard_normal((M, K)) * 0.02, wdt)
     s = (rng.lognormal(0, 0.7, K)).astype(np.float32)
-    v = oracle.quant_values(W, wdt, s)
-    r = oracle.group_rtn(v, bits, group)
     codes, sc, zz = T.ttq_quantize_groups(to_dev(W, wdt), f32_dev(s), bits, group)
-    np.testing.assert_array_equal(host(sc), r["delta"])
-    np.testing.assert_array_equal(host(zz), r["zero"])
-    _check_codes(T, host(codes), r["q"], r["u"], bits, K)
+    _check_rtn(codes, sc, zz, oracle.quant_values(W, wdt, s), bits, group)
 
 
 @pytest.mark.parametrize("bits,group", [(4, 32), (3, 16)])
@@ -154,11 +151,8 @@ def test_quantize_large_weight(T, bits, group):
     rng = np.random.default_rng(77 + bits)
     W = synth.encode(rng.standard_normal((M, K), dtype=np.float32) * 0.01, "bf16")
     s = (rng.lognormal(0, 0.5, K)).astype(np.float32)
-    r = oracle.group_rtn(oracle.quant_values(W, "bf16", s), bits, group)
     codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "bf16"), f32_dev(s), bits, group)
-    np.testing.assert_array_equal(host(sc), r["delta"])
-    np.testing.assert_array_equal(host(zz), r["zero"])
-    _check_codes(T, host(codes), r["q"], r["u"], bits, K)
+    _check_rtn(codes, sc, zz, oracle.quant_values(W, "bf16", s), bits, group)
 
 
 def test_quantize_without_scales_is_plain_rtn(T):
@@ -166,11 +160,12 @@ def test_quantize_without_scales_is_plain_rtn(T):
     M, K = 64, 512
     rng = np.random.default_rng(9)
     W = synth.encode(rng.standard_normal((M, K)) * 0.05, "bf16")
-    r = oracle.group_rtn(oracle.quant_values(W, "bf16", np.ones(K, np.float32)), 4, 32)
     codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "bf16"), None, 4, 32)
-    np.testing.assert_array_equal(host(sc), r["delta"])
-    np.testing.assert_array_equal(host(zz), r["zero"])
-    _check_codes(T, host(codes), r["q"], r["u"], 4, K)
+    v = oracle.quant_values(W, "bf16", np.ones(K, np.float32))
+    _check_rtn(codes, sc, zz, v, 4, 32)
+    # bf16 weights with s = 1 hit exact ties (v / step = k + 1/2) often: the
+    # band admits either code there
+    assert exact_ties(v, oracle.group_rtn(v, 4, 32)["delta"], 32).any()
 
 
 def test_quantize_degenerate_groups(T):
@@ -181,26 +176,45 @@ def test_quantize_degenerate_groups(T):
     W[2] = -0.5                       # constant negative row
     W[3, :32] = np.linspace(0, 1, 32)  # one-sided group
     W[4, 100] = 3.0                   # a lone spike
-    r = oracle.group_rtn(oracle.quant_values(W, "f32", np.ones(K, np.float32)), 3, 32)
     codes, sc, zz = T.ttq_quantize_groups(to_dev(W, "f32"), f32_dev(np.ones(K)), 3, 32)
-    np.testing.assert_array_equal(host(sc), r["delta"])
-    np.testing.assert_array_equal(host(zz), r["zero"])
-    _check_codes(T, host(codes), r["q"], r["u"], 3, K)
+    _check_rtn(codes, sc, zz, oracle.quant_values(W, "f32", np.ones(K, np.float32)), 3, 32)
 
 
-@pytest.mark.parametrize("bits,group,rank", [(2, 32, 16), (3, 16, 8), (4, 64, 5), (5, 32, 32)])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_quantize_nan_groups(T, wdt):
+    # NaN weights: the group range ignores them and a NaN value gets code 0
+    # (the oracle's rule); an all-NaN group takes the zero-range rule (step
+    # 1, zero 0).  Mixed groups with NaN keep their other codes exact.
+    say(f"quantize NaN groups {wdt}")
+    M, K = 16, 512
+    rng = np.random.default_rng(31)
+    Wf = rng.standard_normal((M, K)) * 0.05
+    Wf[0, :32] = np.nan                       # a whole group
+    Wf[1, 5] = np.nan                         # one value of a group
+    Wf[2, 64:128:3] = np.nan                  # scattered over two groups
+    Wf[3, :] = np.nan                         # a whole row
+    Wf[5, 200] = np.nan
+    Wf[5, 201:224] = 0.0                      # NaN among zeros
+    W = synth.encode(Wf, wdt)
+    s = rng.lognormal(0, 0.3, K).astype(np.float32)
+    for bits, group in ((4, 32), (3, 16), (2, 64)):
+        v = oracle.quant_values(W, wdt, s)
+        assert (oracle.group_rtn(v, bits, group)["q"][np.isnan(Wf)] == 0).all()
+        codes, sc, zz = T.ttq_quantize_groups(to_dev(W, wdt), f32_dev(s), bits, group)
+        _check_rtn(codes, sc, zz, v, bits, group)
+        assert (oracle.unpack_codes(host(codes), bits, K)[np.isnan(Wf)] == 0).all()
+
+
+@pytest.mark.parametrize("bits,group,rank", [(2, 32, 16), (3, 16, 8), (4, 64, 5), (5, 32, 32), (4, 32, 48),
+                                            (2, 32, 64)])
 def test_quantize_lowrank_parity(T, bits, group, rank):
     say(f"quantize lowrank bits={bits} group={group} rank={rank}")
     wl, d = _inputs("c5", T=32, K=1024, M=96)
     s = oracle.awq_scales(oracle.stats(d["X"], "bf16"), 32, 0.5, 1e-2)
     B, A = oracle.lowrank_factors(d["W"], "bf16", s, rank)
-    v = oracle.quant_values(d["W"], "bf16", s, B, A)
-    r = oracle.group_rtn(v, bits, group)
     codes, sc, zz = T.ttq_quantize_groups(to_dev(d["W"], "bf16"), f32_dev(s), bits, group,
                                           B=f32_dev(B), A=f32_dev(A))
-    np.testing.assert_array_equal(host(sc), r["delta"])
-    np.testing.assert_array_equal(host(zz), r["zero"])
-    _check_codes(T, host(codes), r["q"], r["u"], bits, 1024)
+    _check_rtn(codes, sc, zz, oracle.quant_values(d["W"], "bf16", s, B, A), bits, group)
 
 
 # ------------------------------------------------------------------ qgemm
@@ -218,6 +232,8 @@ def _qgemm_case(T, key, Tn, K, M, bits, group, xdt, ydt, seed=0):
                     M, bits, group, y_dtype=torch.float32 if ydt == "f32" else torch.bfloat16, ws=ws)
     got = host(Y)
     got = got.astype(np.float64) if ydt == "f32" else bf16_bits_to_f64(got)
+    y_elementwise_check(got, X, xdt, s, r["q"], r["delta"], r["zero"], group,
+                        valu=(Tn <= 4 and K % 128 == 0), y_bf16=(ydt == "bf16"))
     return got, ref
 
 
@@ -359,7 +375,8 @@ def _offset_dev(a: np.ndarray) -> torch.Tensor:
 
 @pytest.mark.parametrize("xdt,rank,a_off,K", [("bf16", 16, False, 512), ("f32", 7, False, 512),
                                               ("bf16", 32, False, 512), ("bf16", 16, True, 512),
-                                              ("bf16", 5, False, 512), ("bf16", 16, False, 4096)])
+                                              ("bf16", 5, False, 512), ("bf16", 16, False, 4096),
+                                              ("bf16", 64, False, 512), ("f32", 40, False, 512)])
 def test_lowrank_add_parity(T, xdt, rank, a_off, K):
     # bf16 X with an aligned A runs Z on the matrix cores; fp32 X or an A
     # that is not 16-byte aligned runs the K-slice kernel.  K = 4096 with 150
@@ -398,7 +415,29 @@ E2E = [
     ("c5-slices", dict(T=300, K=2048, M=256)),
     # few 128 x 256 tiles and K >= 8192: two K slices plus their ordered sum
     ("c4-split", dict(T=260, K=8192, M=302)),
+    # ranks above 32: the GEMM epilogue adds Z B^T in two chunks of ranks
+    ("c5-rank64", dict(T=260, K=512, M=512, rank=64)),
+    ("c5-rank40", dict(T=64, K=512, M=320, rank=40)),
 ]
+
+
+def _check_linear_state(wl, d, st, ref, B=None, A=None):
+    """The prompt state left by ttq_linear: statistics and scales against the
+    oracle, then (whatever the scales) the quantizer's codes, steps and zeros
+    against the oracle's group RTN on the library's own scales."""
+    np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
+    s = host(st["s"])
+    check_scales(s, ref["s"], rtol=S_TOL)
+    check_quant_state(host(st["codes"]), host(st["scale_f16"]), host(st["zero_f16"]), d["W"], wl.wdtype, s,
+                      wl.bits, wl.group, B, A)
+
+
+def _check_y_on_state(wl, d, Y, st, B=None, A=None):
+    """Every element of Y against the projection of the library's own state."""
+    q = oracle.unpack_codes(host(st["codes"]), wl.bits, wl.K)
+    y_elementwise_check(host(Y), d["X"], wl.xdtype, host(st["s"]), q, host(st["scale_f16"]).view(np.float16),
+                        host(st["zero_f16"]).view(np.float16), wl.group, B, A,
+                        valu=(wl.T <= 4 and wl.K % 128 == 0))
 
 
 def _run_linear(T, wl, d, B=None, A=None):
@@ -421,16 +460,11 @@ def test_linear_end_to_end(T, key, sizes):
     ref = oracle.linear(d["X"], wl.xdtype, d["W"], wl.wdtype, wl.bits, wl.group, wl.alpha,
                         wl.lambda_rel, B=B, A=A)
     Y, st = _run_linear(T, wl, d, B, A)
-    np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
-    s = host(st["s"])
-    np.testing.assert_allclose(s, ref["s"], rtol=S_TOL)
-    if np.array_equal(s, ref["s"]):   # identical scales: the quantizer must agree too
-        np.testing.assert_array_equal(host(st["scale_f16"]), ref["delta"])
-        np.testing.assert_array_equal(host(st["zero_f16"]), ref["zero"])
-        _check_codes(T, host(st["codes"]), ref["q"], ref["u"], wl.bits, wl.K)
+    _check_linear_state(wl, d, st, ref, B, A)
     err = rel_fro(host(Y), ref["Y"])
     say(f"  Y rel err {err:.3e}")
     assert err < Y_TOL
+    _check_y_on_state(wl, d, Y, st, B, A)
 
 
 @pytest.mark.parametrize("p,key,sizes", [(1.0, "c2", dict(T=400, K=1024, M=300)),
@@ -446,14 +480,10 @@ def test_linear_moment_p(T, p, key, sizes):
     st = T.linear_state(wl.T, wl.K, wl.M, wl.bits, wl.group)
     Y = T.ttq_linear(to_dev(d["X"], wl.xdtype), to_dev(d["W"], wl.wdtype), wl.bits, wl.group, wl.alpha,
                      wl.lambda_rel, p=p, state=st)
-    np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
+    _check_linear_state(wl, d, st, ref)
     s = host(st["s"])
-    np.testing.assert_allclose(s, ref["s"], rtol=S_TOL)
-    if np.array_equal(s, ref["s"]):
-        np.testing.assert_array_equal(host(st["scale_f16"]), ref["delta"])
-        np.testing.assert_array_equal(host(st["zero_f16"]), ref["zero"])
-        _check_codes(T, host(st["codes"]), ref["q"], ref["u"], wl.bits, wl.K)
     assert rel_fro(host(Y), ref["Y"]) < (Y_TOL if wl.xdtype == "bf16" else 1e-4)
+    _check_y_on_state(wl, d, Y, st)
     # the fused scales equal the standalone call's bit for bit
     s2 = T.ttq_awq_scales(st["ssq"], wl.T, wl.alpha, wl.lambda_rel, p=p)
     np.testing.assert_array_equal(host(s2), s)
@@ -630,3 +660,31 @@ def test_binding_raises_on_bad_arguments(T):
         T.ttq_linear(X, W, 4, 32, 0.5, 1e-2)
     with pytest.raises(TypeError):
         T.ttq_stats(torch.zeros((4, 64)), torch.zeros(64, dtype=torch.float64))
+
+
+def test_side_stream_temporaries(T):
+    # Calls on a stream other than the current one: the binding's default
+    # workspace and outputs are allocated on the launch stream, so work queued
+    # meanwhile on the current stream cannot reuse that memory while the
+    # kernels still run.  The results equal the current-stream call's.
+    say("side-stream launch")
+    wl, d = _inputs("c2", T=300, K=1024, M=288)
+    X, W = to_dev(d["X"], "bf16"), to_dev(d["W"], "bf16")
+    Y0 = T.ttq_linear(X, W, wl.bits, wl.group, wl.alpha, wl.lambda_rel)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for handle in (side, side.cuda_stream):
+        Y1 = T.ttq_linear(X, W, wl.bits, wl.group, wl.alpha, wl.lambda_rel, stream=handle)
+        # the current stream allocates and overwrites memory while side runs
+        junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+        del junk
+        codes, sc, zz = T.ttq_quantize_groups(W, None, 4, 32, stream=handle)
+        outs.append((Y1, codes))
+    side.synchronize()
+    torch.cuda.synchronize()
+    ref_codes = T.ttq_quantize_groups(W, None, 4, 32)[0]
+    for Y1, codes in outs:
+        assert torch.equal(Y1, Y0)
+        assert torch.equal(codes, ref_codes)

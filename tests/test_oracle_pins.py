@@ -316,6 +316,44 @@ def test_rtn_degenerate_groups():
     assert float(r["zero"][1, 1]) == 7.0  # rne(1 / fp16up(2/15)) = rne(7.498)
 
 
+def test_boundary_band_hand_example_value_is_outside():
+    # [TTQ §method b1] group RTN; the acceptance band covers only values
+    # within 1e-4 of a step of a rounding boundary.  In the hand example of
+    # tests/golden/rtn_hand_example.json, v = 0.5 in a group with step
+    # 0.33349609375 gives v / step = 1.49927..., 7.3e-4 of a step below the
+    # boundary 1.5: it lies outside the band, so its code (2) must match
+    # exactly.  No value of that example lies inside the band.
+    g = load_golden("rtn_hand_example.json")
+    r = oracle.group_rtn(np.array([g["v"]], dtype=np.float32), g["bits"], g["group"])
+    u2 = float(r["u"][0, 2])
+    assert abs(u2 - 1.5) == pytest.approx(7.32e-4, abs=1e-6)
+    assert not oracle.boundary_band(r["u"]).any()
+
+
+def test_boundary_band_width_and_quantity():
+    # Values k + 1/2 +- 5e-5 (in units of a step) are inside the band;
+    # +- 2e-4 and 7.3e-4 are outside; integers are outside; negative values
+    # follow the same rule.  The band is computed on v / step, not on v: a
+    # group with step exactly 0.25 (b = 2: range [0, 0.75]) places
+    # v = (1.5 + off) * 0.25 at v / step = 1.5 + off.
+    u = np.array([2.5 + 5e-5, 2.5 - 5e-5, -3.5 + 5e-5, -3.5 - 5e-5, 0.5, 7.5,
+                  2.5 + 2e-4, 2.5 - 2e-4, 1.5 + 7.3e-4, 3.0, -2.0, 0.0])
+    np.testing.assert_array_equal(oracle.boundary_band(u),
+                                  [True] * 6 + [False] * 6)
+    for off, inside in ((5e-5, True), (-5e-5, True), (2e-4, False), (7.3e-4, False)):
+        v = np.array([[0.0, (1.5 + off) * 0.25, 0.75, 0.3]], dtype=np.float32)
+        r = oracle.group_rtn(v, 2, 4)
+        assert float(r["delta"][0, 0]) == 0.25
+        assert bool(oracle.boundary_band(r["u"])[0, 1]) is inside, off
+        assert not oracle.boundary_band(r["u"])[0, [0, 2, 3]].any()
+    # For values spread over many steps, the band holds a fraction 2e-4 of
+    # them (two sides of 1e-4 per boundary): a band ten times too wide or
+    # narrow fails this.
+    rng = np.random.default_rng(0)
+    frac = oracle.boundary_band(rng.uniform(-40.0, 40.0, 10 ** 6)).mean()
+    assert 1.6e-4 < frac < 2.4e-4
+
+
 def test_alpha_zero_reduces_to_plain_rtn_of_w():
     # [TTQ §results] baselines: with alpha = 0 the method is plain group RTN
     wl = synth.workload("c1", T=32, K=256, M=64)
