@@ -77,10 +77,9 @@ typedef enum {
  *   ssq[j] (+)= sum_{t<T} X[t][j]^2, accumulated in fp64.
  *   X: [T][K] fp32 or bf16 (xt), stride ldx >= K.   ssq: [K] fp64, output.
  *   accumulate != 0 adds to the existing ssq (chunked prefill), else
- *   overwrites it.  ws: scratch for at most 32 fp64 partial rows, i.e.
- *   32*K*8 bytes whatever T is (ttq_workspace_bytes covers it; T <= 256
- *   or K > 10176 take a one-kernel path that leaves it unused);
- *   all sums are reduced in a fixed order, so results are bitwise
+ *   overwrites it.  ws, ws_bytes: unused (the reduction runs in one
+ *   kernel without partial sums in memory); any value, NULL included.
+ *   All sums are reduced in a fixed order, so results are bitwise
  *   reproducible run to run.  K must be a multiple of 8.
  */
 ttq_status ttq_stats(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,

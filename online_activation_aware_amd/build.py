@@ -1,6 +1,6 @@
 """Build libttq.so (HIP, gfx950 only) in-tree.
 
-    python -m online_activation_aware_amd.build
+    python -m online_activation_aware_amd.build [source.hip ...]
 
 Compiles every HIP source under csrc/ with hipcc for gfx950 and links them
 into online_activation_aware_amd/libttq.so.  Objects go to _build/.
@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libttq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["stats.hip", "quantize.hip", "qgemm.hip", "qgemv.hip", "gemm_bf16.hip", "lowrank.hip", "factors.hip", "ttq_api.cpp"]
+SOURCES = ["stats.hip", "quantize.hip", "qgemm.hip", "qgemv.hip", "gemm_bf16.hip", "lowrank.hip", "factors.hip",
+           "ttq_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -52,12 +53,15 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, verbose: bool = True) -> str:
-    """Compile all sources and link libttq.so; returns its path."""
+def build(extra: list[str] | None = None, verbose: bool = True, only: list[str] | None = None) -> str:
+    """Compile all sources (or only the named ones, reusing the other objects
+    from an earlier build) and link libttq.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
+    todo = SOURCES if not only else [s for s in SOURCES if s in only]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        list(ex.map(lambda s: _compile(s, extra), todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -70,4 +74,6 @@ def build(extra: list[str] | None = None, verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    # python -m online_activation_aware_amd.build [source.hip ...]: rebuild
+    # only the named sources (others from _build/), then link.
+    build(only=sys.argv[1:] or None)

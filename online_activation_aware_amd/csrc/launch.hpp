@@ -30,20 +30,16 @@ inline hipError_t launch_kernel(F kern, dim3 grid, dim3 block, size_t lds, hipSt
     return hipGetLastError();
 }
 
-// Token-chunk split of the statistics reduction: returns the number of
-// chunks (fp64 partial rows) and the rows per chunk.
-int stats_chunks(int64_t T, int64_t K, int* rows_per_chunk);
 // K-slice split of the low-rank Z = A X pass.
 int lowrank_slices(int64_t T, int64_t K, int64_t* slice_len);
 
-// At most this many fp64 partial rows of K channels in the stats workspace.
-constexpr int kMaxStatsChunks = 32;
-// bsum (optional, ceil(K/64) doubles): per-64-channel block sums of
-// c = ssq / T, from which the quantizer forms lambda = lambda_rel * mean(c).
-// p: moment order of the statistic, sum |x|^p (2: sums of squares).
+// Statistics in one launch (no workspace).  bsum (optional, ceil(K/16)
+// doubles): per-16-channel block sums of c = ssq / T, from which the
+// quantizer forms lambda = lambda_rel * mean(c).  p: moment order of the
+// statistic, sum |x|^p (2: sums of squares).
 hipError_t launch_stats(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, double* ssq,
-                        int accumulate, double* part, hipStream_t st, double* bsum = nullptr,
-                        StageTimer tm = {}, double p = 2.0);
+                        int accumulate, hipStream_t st, double* bsum = nullptr, StageTimer tm = {},
+                        double p = 2.0);
 hipError_t launch_awq_scales(const double* ssq, int64_t n_tokens, int64_t K, float alpha,
                              float lambda_rel, float p, float* s, hipStream_t st);
 // Scales evaluated inside the quantizer from the statistics (instead of a

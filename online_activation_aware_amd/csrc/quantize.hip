@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
         __shared__ float ssc[kQChans];
         __shared__ double lam_s;
         if (wave == 0) {
-            const double tot = blocks_total(qs.bsum, (K + 63) / 64, lane);
+            const double tot = blocks_total(qs.bsum, (K + kBlockCh - 1) / kBlockCh, lane);
             if (lane == 0) lam_s = qs.lambda_rel * (tot / (double)K);
         }
         __syncthreads();

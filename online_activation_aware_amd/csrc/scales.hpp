@@ -1,18 +1,19 @@
 // Shrunk AWQ scale arithmetic shared by the kernels that evaluate it, so that
 // every path produces bitwise the same lambda and s.
 //
-// [TTQ §method b2-b4]: c[j] = ssq[j] / n (second moment of channel j over the
-// prompt); lambda = lambda_rel * mean_j c[j] (shrinkage C + lambda I);
-// s[j] = (c[j] + lambda)^(alpha / 2), in fp64, rounded once to fp32, and 1
-// where c[j] + lambda == 0.
+// [TTQ §method b2-b4]: c[j] = ssq[j] / n (moment of order p of channel j over
+// the prompt; p = 2: the second moment); lambda = lambda_rel * mean_j c[j]
+// (shrinkage C + lambda I); s[j] = (c[j] + lambda)^(alpha / p), in fp64,
+// rounded once to fp32, and 1 where c[j] + lambda == 0.
 #pragma once
 
 #include "common.hpp"
 
 namespace ttq {
 
-// Channel blocks of 64 for the shrinkage mean: at most 4096 (K <= 2^18).
-constexpr int kMaxBlocks = 4096;
+// Channel blocks of 16 for the shrinkage mean: at most 16384 (K <= 2^18).
+constexpr int kBlockCh = 16;
+constexpr int kMaxBlocks = (1 << 18) / kBlockCh;
 
 // Wave-wide sum in a fixed butterfly order: every lane receives the same,
 // run-to-run reproducible value.
@@ -22,12 +23,20 @@ __device__ __forceinline__ double wave_sum_fixed(double v) {
     return v;
 }
 
-// Channel-block sum of the second moments: block b covers channels
-// 64 b .. 64 b + 63 (lane l <-> channel 64 b + l; missing channels count 0).
+// Sum over each aligned run of 16 lanes in a fixed butterfly (xor 8, 4, 2,
+// 1): every lane of the run receives the same value.  All 64 lanes call it.
+__device__ __forceinline__ double seg16_sum_fixed(double v) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Block sum of the second moments: block b covers channels 16 b .. 16 b + 15;
+// lane l of a 16-lane run holds channel 16 b + l (missing channels count 0).
 __device__ __forceinline__ double cblock_sum(const double* __restrict__ ssq, int64_t b, int64_t K,
-                                             double tn, int lane) {
-    const int64_t j = 64 * b + lane;
-    return wave_sum_fixed(j < K ? ssq[j] / tn : 0.0);
+                                             double tn, int l16) {
+    const int64_t j = (int64_t)kBlockCh * b + l16;
+    return seg16_sum_fixed(j < K ? ssq[j] / tn : 0.0);
 }
 
 // Total of the nb block sums in a fixed order (one full wave calls this): lane

@@ -111,12 +111,6 @@ ttq_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
     return TTQ_OK;
 }
 
-// The statistics use at most kMaxStatsChunks token chunks whatever T is, so
-// one workspace fits every prompt length.
-size_t ws_stats(int64_t T, int64_t K) {
-    if (T <= 0) return 0;
-    return round_up((size_t)ttq::kMaxStatsChunks * (size_t)K * sizeof(double));
-}
 // Prompt-sized projections stage the dequantized weight (M x K bf16) in the
 // workspace; the size is requested whenever T allows that path.
 size_t ws_qgemm(int64_t T, int64_t K, int64_t M) {
@@ -147,9 +141,9 @@ StateLayout state_layout(int64_t T, int64_t K, int64_t M, int bits, int group, i
     L.codes = off;   off += round_up((size_t)M * (size_t)(K * bits / 32) * sizeof(int32_t));
     L.scale = off;   off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
     L.zero = off;    off += round_up((size_t)M * (size_t)(K / group) * sizeof(uint16_t));
-    L.bsum = off;    off += round_up((size_t)((K + 63) / 64) * sizeof(double));
+    L.bsum = off;    off += round_up((size_t)((K + 15) / 16) * sizeof(double));
     L.scratch = off;
-    size_t scratch = ws_stats(T, K);
+    size_t scratch = 0;
     // prompt-sized projections: the dequantized weight, then Z = X A^T for
     // the low-rank epilogue
     const size_t proj = ws_qgemm(T, K, M) + (rank > 0 && T > 0 ? round_up((size_t)ttq::lowrank_zm_parts(T, K) *
@@ -199,11 +193,11 @@ ttq_status ttq_stats_p(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
     TTQ_REQUIRE(K > 0 && K <= kMaxK && K % 8 == 0, "K must be a positive multiple of 8, at most 2^18");
     if (ttq_status e = check_matrix("X", X, xt, T, K, ldx)) return e;
     TTQ_REQUIRE(ssq != nullptr && aligned(ssq, 8), "ssq: null or not 8-byte aligned");
-    const size_t need = T > 0 ? ws_stats(T, K) : 0;
-    if (ttq_status e = check_ws(ws, ws_bytes, need)) return e;
+    (void)ws;
+    (void)ws_bytes;
     if (T == 0 && accumulate) return TTQ_OK;
-    return device_status(ttq::launch_stats(X, xt == TTQ_F32, T, K, ldx, ssq, accumulate,
-                                           (double*)ws, as_stream(stream), nullptr, {}, (double)p),
+    return device_status(ttq::launch_stats(X, xt == TTQ_F32, T, K, ldx, ssq, accumulate, as_stream(stream),
+                                           nullptr, {}, (double)p),
                          "ttq_stats launch");
 }
 
@@ -474,12 +468,11 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
     double* ssq = a->ssq ? a->ssq : (double*)(w + L.ssq);
     double* bsum = (double*)(w + L.bsum);
     hipStream_t st = as_stream(stream);
-    // Statistics (sums of |x|^p); the reduction also leaves the 64-channel
+    // Statistics (sums of |x|^p); the reduction also leaves the 16-channel
     // block sums of c.
     const StageMarks sm{a->stage_events, st};
-    if (ttq_status e = device_status(ttq::launch_stats(a->X, a->xt == TTQ_F32, a->T, a->K, a->ldx, ssq, 0,
-                                                       (double*)(w + L.scratch), st, bsum, sm.timer(0),
-                                                       (double)a->p),
+    if (ttq_status e = device_status(ttq::launch_stats(a->X, a->xt == TTQ_F32, a->T, a->K, a->ldx, ssq, 0, st,
+                                                       bsum, sm.timer(0), (double)a->p),
                                      "stats"))
         return e;
     return linear_layer(a, ssq, bsum, w, L, st);
@@ -487,7 +480,7 @@ ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void*
 
 // Shared statistics: [ssq K fp64 | block sums] at the head of the workspace,
 // then one layer's state and scratch at a time (layers run in order).
-static size_t shared_head(int64_t K) { return round_up((size_t)K * 8) + round_up((size_t)((K + 63) / 64) * 8); }
+static size_t shared_head(int64_t K) { return round_up((size_t)K * 8) + round_up((size_t)((K + 15) / 16) * 8); }
 
 size_t ttq_linear_shared_workspace_bytes(const ttq_linear_args* layers, int n) {
     if (layers == nullptr || n < 1) return 0;
@@ -525,9 +518,8 @@ ttq_status ttq_linear_shared(const ttq_linear_args* layers, int n, void* ws, siz
     double* bsum = (double*)(w + round_up((size_t)a0->K * 8));
     char* wl = w + head;
     hipStream_t st = as_stream(stream);
-    const StateLayout L0 = state_layout(a0->T, a0->K, a0->M, a0->bits, a0->group, a0->rank);
-    if (ttq_status e = device_status(ttq::launch_stats(a0->X, a0->xt == TTQ_F32, a0->T, a0->K, a0->ldx, ssq, 0,
-                                                       (double*)(wl + L0.scratch), st, bsum, {}, (double)a0->p),
+    if (ttq_status e = device_status(ttq::launch_stats(a0->X, a0->xt == TTQ_F32, a0->T, a0->K, a0->ldx, ssq, 0, st,
+                                                       bsum, {}, (double)a0->p),
                                      "stats"))
         return e;
     for (int i = 0; i < n; ++i) {

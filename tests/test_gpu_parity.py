@@ -48,7 +48,8 @@ def _check_rtn(got_codes, got_delta, got_zero, v, bits, group):
 # ------------------------------------------------------------------ stats
 
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
-@pytest.mark.parametrize("Tn,K", [(1, 512), (77, 1000), (300, 2056), (1031, 4104), (600, 10304)])
+@pytest.mark.parametrize("Tn,K", [(1, 512), (77, 1000), (300, 2056), (1031, 4104), (600, 10304), (5000, 24),
+                                  (3, 8), (2048, 4096), (1024, 14336)])
 def test_stats_parity(T, xdt, Tn, K):
     say(f"stats xdt={xdt} T={Tn} K={K}")
     rng = np.random.default_rng(Tn + K)
