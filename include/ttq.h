@@ -306,6 +306,24 @@ ttq_status ttq_linear_shared(const ttq_linear_args* layers, int n, void* ws, siz
 /* Workspace bytes for ttq_linear_shared (0 when some layer's sizes are not accepted). */
 size_t ttq_linear_shared_workspace_bytes(const ttq_linear_args* layers, int n);
 
+/*
+ * ttq_linear_noalloc — ttq_linear without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The library allocates
+ * nothing here either: the workspace is a device array inside the library,
+ * TTQ_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * process ends.  Arguments, results and the other checks are those of
+ * ttq_linear; a layer whose ttq_workspace_bytes(T, K, M, bits, group, rank)
+ * exceeds TTQ_NOALLOC_SCRATCH_BYTES returns TTQ_ERR_INVALID (give the state
+ * outputs ssq, s, codes, scale_f16, zero_f16 to keep them out of the array).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from threads without ordering) race and give
+ * undefined results.  The array's address is resolved on the first call on
+ * each device (TTQ_ERR_DEVICE if that fails).
+ */
+#define TTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ttq_status ttq_linear_noalloc(const ttq_linear_args* args, void* stream);
+
 /* Static text for a status code. */
 const char* ttq_status_str(int status);
 

@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libttq.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["stats.hip", "quantize.hip", "qgemm.hip", "qgemv.hip", "gemm_bf16.hip", "lowrank.hip", "factors.hip",
-           "ttq_api.cpp"]
+           "noalloc.hip", "ttq_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

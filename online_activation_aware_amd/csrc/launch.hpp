@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ttq.h"
+
 namespace ttq {
 
 // Stage timing: the first kernel of a stage records `start` as it starts and
@@ -124,5 +126,11 @@ FactorsLayout factors_layout(int64_t M, int64_t K, int l);
 bool factors_supported(bool wf32, int64_t M, int64_t K, int l, int rank);
 hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, const float* s, const float* om,
                           int l, int q, int rank, float* B, float* A, char* ws, hipStream_t st);
+
+// ttq_linear's argument checks (clearing the calling thread's error text
+// first) and the workspace bytes the call needs (0 for an empty call).
+ttq_status linear_check(const ttq_linear_args* a, size_t* need);
+// Record `msg` as the calling thread's last error text; returns st.
+ttq_status set_error(ttq_status st, const char* msg);
 
 }  // namespace ttq

@@ -458,6 +458,23 @@ static ttq_status linear_layer(const ttq_linear_args* a, const double* ssq, cons
     return markers(3);
 }
 
+}  // extern "C"
+
+namespace ttq {
+
+ttq_status linear_check(const ttq_linear_args* a, size_t* need) {
+    g_last_error.clear();
+    if (ttq_status e = check_linear(a)) return e;
+    *need = a->T == 0 ? 0 : state_layout(a->T, a->K, a->M, a->bits, a->group, a->rank).total;
+    return TTQ_OK;
+}
+
+ttq_status set_error(ttq_status st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace ttq
+
+extern "C" {
+
 ttq_status ttq_linear(const ttq_linear_args* a, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (ttq_status e = check_linear(a)) return e;

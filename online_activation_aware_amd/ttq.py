@@ -23,7 +23,7 @@ TTQ_F32, TTQ_BF16 = 0, 1
 EXPORTS = ("ttq_stats", "ttq_stats_p", "ttq_awq_scales", "ttq_quantize_groups", "ttq_qgemm", "ttq_qgemm_batched",
            "ttq_lowrank_add", "ttq_lowrank_factors", "ttq_lowrank_factors_workspace_bytes",
            "ttq_workspace_bytes", "ttq_linear", "ttq_linear_shared", "ttq_linear_shared_workspace_bytes",
-           "ttq_status_str", "ttq_last_error")
+           "ttq_linear_noalloc", "ttq_status_str", "ttq_last_error")
 
 
 class TTQError(RuntimeError):
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "ttq_lowrank_factors": [vp, i32, i64, i64, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
         "ttq_lowrank_factors_workspace_bytes": [i64, i64, i32],
         "ttq_linear": [ctypes.POINTER(LinearArgs), vp, sz, vp],
+        "ttq_linear_noalloc": [ctypes.POINTER(LinearArgs), vp],
         "ttq_linear_shared": [ctypes.POINTER(LinearArgs), i32, vp, sz, vp],
         "ttq_linear_shared_workspace_bytes": [ctypes.POINTER(LinearArgs), i32],
         "ttq_status_str": [i32],
@@ -337,6 +338,30 @@ def ttq_linear(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: f
     )
     wp, wn = _ws(ws, X.device)
     _check(lib().ttq_linear(ctypes.byref(a), wp, wn, _stream(stream)))
+    return Y
+
+
+@_on_launch_stream
+def ttq_linear_noalloc(X: torch.Tensor, W: torch.Tensor, bits: int, group: int, alpha: float,
+                       lambda_rel: float, Y: torch.Tensor, p: float = 2.0, B: Optional[torch.Tensor] = None,
+                       A: Optional[torch.Tensor] = None, state: Optional[dict] = None,
+                       stream=None) -> torch.Tensor:
+    """ttq_linear with the library's own scratch array as the workspace (the
+    call allocates nothing; Y and the optional state tensors come from the
+    caller)."""
+    T, K = X.shape
+    M = W.shape[0]
+    st = state or {}
+    a = LinearArgs(
+        X=_dev(X, "X"), xt=_dtype_code(X), T=T, K=K, ldx=_ld(X, "X"),
+        W=_dev(W, "W"), wt=_dtype_code(W), M=M, ldw=_ld(W, "W"),
+        alpha=alpha, lambda_rel=lambda_rel, p=p, bits=bits, group=group,
+        B=_dev(B, "B"), A=_dev(A, "A"), rank=0 if B is None else B.shape[1],
+        Y=_dev(Y, "Y"), yt=_dtype_code(Y), ldy=_ld(Y, "Y"),
+        ssq=_dev(st.get("ssq"), "ssq"), s=_dev(st.get("s"), "s"), codes=_dev(st.get("codes"), "codes"),
+        scale_f16=_dev(st.get("scale_f16"), "scale_f16"), zero_f16=_dev(st.get("zero_f16"), "zero_f16"),
+        stage_events=None)
+    _check(lib().ttq_linear_noalloc(ctypes.byref(a), _stream(stream)))
     return Y
 
 
