@@ -1,217 +1,249 @@
-// Group-wise RTN of the scaled (residual) weight, packed into int32 words.
+// Group-wise RTN of the scaled weight, packed into int32 words.
 //
 // [TTQ §method b1] group-wise RTN; [TTQ §method b2] the weight is scaled by the
-// AWQ scale of its input channel; [TTQ §method b5] with dynamic low-rank factors
-// the residual W - B A is what gets quantized.
+// AWQ scale of its input channel.  (With dynamic low-rank factors, [TTQ
+// §method b5], the residual W - B A is quantized by quantize_lr.hip.)
 //
-// Mapping: a workgroup (4 waves) owns a strip of 512 input channels and a
-// block of output rows; lane l owns 8 consecutive channels (one 16-byte bf16
-// load, two for fp32), so a group of g channels spans g/8 adjacent lanes and
-// its min/max needs log2(g/8) DPP lane exchanges.  Four adjacent lanes hold
-// 32 codes = `bits` int32 words, assembled with quad broadcasts and written
-// by the first `bits` lanes of the quad.  With low-rank factors, the strip of A
-// (up to 32 ranks x 512 fp32) is staged once in LDS and reused for every row;
-// ranks 32..63 are read from global memory.
+// Mapping: a workgroup (4 waves) owns a strip of 1024 input channels and walks
+// blocks of output rows; lane l owns 16 consecutive channels (two 16-byte
+// loads of bf16, four of fp32), so a group of g channels spans g/16 adjacent
+// lanes and its min/max needs log2(g/16) DPP lane exchanges.  The group's
+// step, zero point and 1/step are formed once per lane and row and serve its
+// 16 weights.
+//
+// Arithmetic (rtn.hpp):
+//  - v = fp32(w * s);
+//  - step: fp32(mx - mn) / (2^b - 1) by a multiply with the rounded
+//    reciprocal of the constant and one fma correction, which equals the
+//    correctly rounded division for every finite operand (checked
+//    exhaustively over all non-negative fp32 values for 3, 7, 15 and 31);
+//    then fp16 rounded toward +inf; zero = rne(-mn / step) by an IEEE
+//    division;
+//  - code: rne(v * (1/step)) + zero, clamped to [0, 2^b - 1].  One fma
+//    forms v * (1/step) + (1.5 * 2^23 + zero); the fp32 spacing there is 1,
+//    so the result holds the rounded code in its low significand bits; the
+//    clamp is one v_med3 (a NaN value gives the lower bound, code 0), and the
+//    code is the low bits of the result's bit pattern.  v * (1/step)
+//    differs from v / step by a few ulps, and an exact tie (v / step =
+//    k + 1/2) goes to whichever side that error puts it, with zero already
+//    added: only values within ~1e-6 of a step of a rounding boundary can be
+//    decided differently from the oracle.
+//  - packing: a lane's 16 codes form 16 * b bits of its row's stream; each
+//    code's bit pattern (1.5 * 2^23 + code) is shifted into place with one
+//    shift-and-add, and the shifted copies of 1.5 * 2^23 are subtracted as a
+//    compile-time constant per word.  For odd b, lane pairs join their
+//    fields (96 or 160 bits = 3 or 5 words) after one DPP exchange.
 //
 // Optionally the kernel also writes the dequantized weight of [TTQ §method b1]
 // (QDQ) with the input scale folded back, w~ = bf16(((code - zero) * step) *
 // (1/s)), dense [M][K] bf16: the operand of the prompt-sized projection, so
-// that the codes need not be read and expanded a second time.
+// that the codes need not be read and expanded a second time.  (code - zero)
+// comes out exactly as sum - (1.5 * 2^23 + zero).
 #include <atomic>
-#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant_launch.hpp"
+#include "rtn.hpp"
 #include "scales.hpp"
 
 namespace ttq {
 
 constexpr int kQThreads = 256;
-constexpr int kQChans = kWave * 8;
-constexpr int kQLdsRanks = 32;       // ranks of A staged in LDS (64 KB)
+constexpr int kLaneCh = 16;                // channels per lane
+constexpr int kQChans = kWave * kLaneCh;   // channels per strip (workgroup)
 
-// Workgroups of one quantizer kernel resident at once, per device and per
-// number of A ranks staged in LDS (0 = not yet queried).
-constexpr int kMaxDevices = 64;
-struct OccMemo {
-    std::atomic<int> resident[kMaxDevices][kQLdsRanks + 1];
+// Sum of the shifted copies of kMagicBits in word wd of a lane's field
+// (codes whose first bit lies in that word), modulo 2^32.
+template <int BITS>
+__device__ __forceinline__ constexpr uint32_t magic_sum(int wd) {
+    uint32_t c = 0;
+    for (int i = 0; i < kLaneCh; ++i) {
+        const int sh = BITS * i - 32 * wd;
+        if (sh >= 0 && sh < 32) c += kMagicBits << sh;
+    }
+    return c;
+}
+
+// The 16 * BITS bits of one lane's codes (code i at bits [BITS i, BITS i +
+// BITS)) as NW words, the last one partial for odd BITS.  qb holds the bit
+// patterns kMagicBits + code.  A code that straddles two words puts its high
+// bits at the bottom of the next word.
+template <int BITS>
+struct LaneField {
+    static constexpr int NW = (kLaneCh * BITS + 31) / 32;
+    uint32_t w[NW];
 };
 
-// Cross-lane moves through DPP (they run in the VALU pipeline, no LDS round
-// trip).  Quad permutations: lane i of each quad reads lane perm[i]
-// (control perm0 | perm1 << 2 | perm2 << 4 | perm3 << 6); row mirrors
-// reverse 8 or 16 lanes.
-constexpr int kDppQuadXor1 = 0xB1;     // [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4E;     // [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;  // lane l of 8 <- lane 7 - l
-constexpr int kDppMirror = 0x140;      // lane l of 16 <- lane 15 - l
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(float, dpp_u<CTRL>(__builtin_bit_cast(uint32_t, x)));
-}
-
-// min/max over the GL = GROUP/8 lanes of a group (aligned runs of GL lanes).
-template <int GL>
-__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
-    static_assert(GL == 2 || GL == 4 || GL == 8 || GL == 16, "lanes per group");
-    mn = fminf(mn, dpp_f<kDppQuadXor1>(mn));
-    mx = fmaxf(mx, dpp_f<kDppQuadXor1>(mx));
-    if constexpr (GL >= 4) {
-        mn = fminf(mn, dpp_f<kDppQuadXor2>(mn));
-        mx = fmaxf(mx, dpp_f<kDppQuadXor2>(mx));
+template <int BITS>
+__device__ __forceinline__ LaneField<BITS> pack_lane(const uint32_t (&qb)[kLaneCh]) {
+    LaneField<BITS> f;
+#pragma unroll
+    for (int wd = 0; wd < LaneField<BITS>::NW; ++wd) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < kLaneCh; ++i) {
+            const int sh = BITS * i - 32 * wd;
+            if (sh >= 32 || sh + BITS <= 0) continue;
+            if (sh >= 0) acc += qb[i] << sh;                          // shift-and-add
+            else acc += (qb[i] - kMagicBits) >> (-sh);                // high bits of a straddling code
+        }
+        f.w[wd] = acc - magic_sum<BITS>(wd);
     }
-    if constexpr (GL >= 8) {             // each quad holds its own range: pair it with the mirrored quad
-        mn = fminf(mn, dpp_f<kDppHalfMirror>(mn));
-        mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
-    }
-    if constexpr (GL >= 16) {
-        mn = fminf(mn, dpp_f<kDppMirror>(mn));
-        mx = fmaxf(mx, dpp_f<kDppMirror>(mx));
-    }
+    return f;
 }
 
-// Group RTN of one lane's 8 values and packing of the quad's 32 codes.
-// All 64 lanes of the wave must call this together (cross-lane moves).
+// Group RTN of one lane's 16 values and the stores of its codes, step, zero
+// and (optionally) dequantized weights.  All 64 lanes of the wave must call
+// this together (cross-lane moves).
 template <int BITS, int GROUP>
-__device__ __forceinline__ void quantize_and_store(const float (&v)[8], bool active, int lane, int64_t cu,
+__device__ __forceinline__ void quantize_and_store(const float (&v)[kLaneCh], bool active, int lane, int64_t cu,
                                                    int64_t col, int64_t o, int64_t words_per_row,
                                                    int64_t groups_per_row, uint32_t* __restrict__ codes,
                                                    uint16_t* __restrict__ scale, uint16_t* __restrict__ zero,
-                                                   const float (&sinv)[8], uint16_t* __restrict__ wq, int64_t K) {
-    constexpr float QMAX = (float)((1 << BITS) - 1);
-    constexpr int GL = GROUP / 8;                 // lanes per group
-    // Group range (NaN ignored: v_min/v_max return the non-NaN operand).
+                                                   const float (&sinv)[kLaneCh], uint16_t* __restrict__ wq,
+                                                   int64_t K) {
+    constexpr int GL = GROUP / kLaneCh;           // lanes per group
     float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+    for (int i = 1; i < kLaneCh; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
     group_minmax<GL>(mn, mx);
-    mn = fminf(0.0f, mn);
-    mx = fmaxf(0.0f, mx);
-    const float d32 = (mx - mn) / QMAX;           // correctly rounded
-    const uint16_t dh = d32 == 0.0f ? (uint16_t)0x3C00 : f32_to_f16_up(d32);
-    const float df = f16_to_f32(dh);
-    const float z = fminf(fmaxf(rintf((-mn) / df), 0.0f), QMAX);
-    // Codes decided on v * (1/step) (v_rcp_f32, <= 1 ulp): only values within
-    // ~1e-7 of a step from a rounding boundary can differ from a division.
-    const float inv = __builtin_amdgcn_rcpf(df);
+    const GroupStep g = group_step<BITS>(mn, mx);
+    const float mz = kMagic + g.z;                // exact
 
-    // 8 codes of 8*BITS bits; a NaN value gives NaN + z, which the clamp's
-    // v_max_f32 turns into 0.
-    typedef typename std::conditional<(8 * BITS <= 32), uint32_t, uint64_t>::type field_t;
-    field_t field = 0;
-    float qv[8];
+    // Codes as kMagic + code (exact integers in fp32).
+    float qm[kLaneCh];
+    uint32_t qb[kLaneCh];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q = fminf(fmaxf(rintf(v[i] * inv) + z, 0.0f), QMAX);
-        qv[i] = q;
-        field |= (field_t)(uint32_t)q << (BITS * i);
+    for (int i = 0; i < kLaneCh; ++i) {
+        qm[i] = code_magic<BITS>(v[i], g, mz);
+        qb[i] = __builtin_bit_cast(uint32_t, qm[i]);
     }
     if (wq != nullptr && active) {
-        // (q - z) * step is exact in fp32 (a small integer times an fp16 value).
-        u32x4 pk;
+        // (code - zero) * step is exact in fp32 (a small integer times an fp16 value).
+        u32x4 pk0, pk1;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            pk[p] = pack_bf16x2(((qv[2 * p] - z) * df) * sinv[2 * p], ((qv[2 * p + 1] - z) * df) * sinv[2 * p + 1]);
-        *(u32x4*)(wq + o * K + col) = pk;
+        for (int p = 0; p < 4; ++p) {
+            pk0[p] = pack_bf16x2(((qm[2 * p] - mz) * g.df) * sinv[2 * p],
+                                 ((qm[2 * p + 1] - mz) * g.df) * sinv[2 * p + 1]);
+            pk1[p] = pack_bf16x2(((qm[8 + 2 * p] - mz) * g.df) * sinv[8 + 2 * p],
+                                 ((qm[9 + 2 * p] - mz) * g.df) * sinv[9 + 2 * p]);
+        }
+        u32x4* dst = (u32x4*)(wq + o * K + col);
+        dst[0] = pk0;
+        dst[1] = pk1;
     }
 
-    // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words; every lane
-    // of the quad receives the quad's four fields by quad broadcasts.
-    uint64_t fq[4];
-    {
-        const uint32_t lo = (uint32_t)field;
-        fq[0] = dpp_u<0x00>(lo);
-        fq[1] = dpp_u<0x55>(lo);
-        fq[2] = dpp_u<0xAA>(lo);
-        fq[3] = dpp_u<0xFF>(lo);
-        if constexpr (8 * BITS > 32) {
-            const uint32_t hi = (uint32_t)((uint64_t)field >> 32);
-            fq[0] |= (uint64_t)dpp_u<0x00>(hi) << 32;
-            fq[1] |= (uint64_t)dpp_u<0x55>(hi) << 32;
-            fq[2] |= (uint64_t)dpp_u<0xAA>(hi) << 32;
-            fq[3] |= (uint64_t)dpp_u<0xFF>(hi) << 32;
+    const LaneField<BITS> f = pack_lane<BITS>(qb);
+    if constexpr ((BITS & 1) == 0) {
+        // 16 b bits = b/2 whole words per lane.
+        if (active) {
+            uint32_t* wrow = codes + o * words_per_row + cu * (BITS / 2);
+            if constexpr (BITS == 2) {
+                wrow[0] = f.w[0];
+            } else {
+                u32x2 pr = {f.w[0], f.w[1]};
+                *(u32x2*)wrow = pr;
+            }
+        }
+    } else {
+        // Odd b: lanes 2m and 2m + 1 hold 16 b bits each (the last word
+        // half full); their joint 32 b bits are b whole words.  Each lane
+        // receives its partner's field.
+        constexpr int NW = LaneField<BITS>::NW;   // 2 (b = 3) or 3 (b = 5)
+        static_assert((kLaneCh * BITS) % 32 == 16, "odd bit widths leave half a word per lane");
+        uint32_t pw[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) pw[k] = dpp_u<kDppQuadXor1>(f.w[k]);
+        const bool even = (lane & 1) == 0;
+        uint32_t Lw[NW], Rw[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            Lw[k] = even ? f.w[k] : pw[k];
+            Rw[k] = even ? pw[k] : f.w[k];
+        }
+        // the pair's words: L0 .. L(NW-2), L(NW-1) | R0 << 16, R0 >> 16 | R1 << 16, ...
+        uint32_t pair[BITS];
+#pragma unroll
+        for (int k = 0; k < NW - 1; ++k) pair[k] = Lw[k];
+        pair[NW - 1] = (Lw[NW - 1] & 0xFFFFu) | (Rw[0] << 16);
+#pragma unroll
+        for (int k = 1; k < NW; ++k) pair[NW - 1 + k] = (Rw[k - 1] >> 16) | (Rw[k] << 16);
+        if (active) {
+            uint32_t* wrow = codes + o * words_per_row + (cu >> 1) * BITS;
+            // even lane: the first NW words, odd lane: the remaining BITS - NW
+#pragma unroll
+            for (int k = 0; k < BITS; ++k)
+                if ((k < NW) == even) wrow[k] = pair[k];
         }
     }
-    auto word = [&](int j) -> uint32_t {
-        uint32_t wv = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int off = 8 * BITS * k - 32 * j;
-            if (off >= 32 || off + 8 * BITS <= 0) continue;
-            wv |= off >= 0 ? (uint32_t)(fq[k] << off) : (uint32_t)(fq[k] >> (-off));
-        }
-        return wv;
-    };
-    if (active) {
-        const int j = lane & 3;
-        uint32_t* wrow = codes + o * words_per_row + (cu >> 2) * BITS;
-        if (j < BITS) wrow[j] = word(j);
-        if (BITS > 4 && j == 0) wrow[4] = word(4);
-        if ((cu % GL) == 0) {
-            const int64_t gi = o * groups_per_row + col / GROUP;
-            scale[gi] = dh;
-            zero[gi] = f32_to_f16_rne(z);
-        }
+    if (active && (cu % GL) == 0) {
+        const int64_t gi = o * groups_per_row + col / GROUP;
+        scale[gi] = g.dh;
+        zero[gi] = f32_to_f16_rne(g.z);
     }
 }
 
-// Row batch held in registers: raw bf16 (one 16-byte vector) or fp32 (two).
+// Row batch held in registers: 16 raw bf16 (two 16-byte vectors) or fp32
+// (four).
 template <bool WF32>
 struct RawRow {
-    u32x4 a;
-    u32x4 b;
+    u32x4 a[WF32 ? 4 : 2];
 };
 
+// Ordinary (cached) loads: each load instruction of a wave uses half of
+// every line it touches (lanes 32 or 64 bytes apart), and the next
+// instruction takes the other half from the cache.
 template <bool WF32>
 __device__ __forceinline__ void load_row(RawRow<WF32>& r, const void* W, int64_t o, int64_t ldw, int64_t col) {
     if constexpr (WF32) {
         const u32x4* p = (const u32x4*)((const float*)W + o * ldw + col);
-        r.a = ld_nc(p);
-        r.b = ld_nc(p + 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.a[k] = p[k];
     } else {
-        r.a = ld_nc((const u32x4*)((const uint16_t*)W + o * ldw + col));
+        const u32x4* p = (const u32x4*)((const uint16_t*)W + o * ldw + col);
+        r.a[0] = p[0];
+        r.a[1] = p[1];
     }
 }
 
 template <bool WF32>
-__device__ __forceinline__ void unpack_row(const RawRow<WF32>& r, float (&w)[8]) {
+__device__ __forceinline__ void zero_row(RawRow<WF32>& r) {
+#pragma unroll
+    for (int k = 0; k < (WF32 ? 4 : 2); ++k) r.a[k] = u32x4{0u, 0u, 0u, 0u};
+}
+
+template <bool WF32>
+__device__ __forceinline__ void unpack_row(const RawRow<WF32>& r, float (&w)[kLaneCh]) {
     if constexpr (WF32) {
         // Whole-vector casts: this compiler mis-lowers a bit cast whose operand
         // is a single vector element (it reads element 0).
-        const f32x4 fa = __builtin_bit_cast(f32x4, r.a), fb = __builtin_bit_cast(f32x4, r.b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = fa[i];
-            w[4 + i] = fb[i];
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 fa = __builtin_bit_cast(f32x4, r.a[k]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * k + i] = fa[i];
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[2 * i] = bf16lo_to_f32(r.a[i]);
-            w[2 * i + 1] = bf16hi_to_f32(r.a[i]);
-        }
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[8 * k + 2 * i] = bf16lo_to_f32(r.a[k][i]);
+                w[8 * k + 2 * i + 1] = bf16hi_to_f32(r.a[k][i]);
+            }
     }
 }
 
-template <int BITS, int GROUP, bool WF32, bool LOWRANK, bool SFUSE, bool RB4>
+template <int BITS, int GROUP, bool WF32, bool SFUSE>
 __global__ __launch_bounds__(kQThreads) void k_quantize(
     const void* __restrict__ W, int64_t M, int64_t K, int64_t ldw, const float* __restrict__ s,
-    const float* __restrict__ B, const float* __restrict__ A, int rank, int rows_per_block,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero,
     uint16_t* __restrict__ wq, QScaleSrc qs) {
-    // [min(rank, kQLdsRanks)][kQChans] when LOWRANK (16-byte reads); ranks
-    // beyond kQLdsRanks are read from A in global memory (L2-resident).
-    extern __shared__ __attribute__((aligned(16))) float sA[];
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // row addressing stays scalar
-    const int64_t cu = (int64_t)blockIdx.x * kWave + lane;   // 8-channel unit in the row
-    const int64_t col = cu * 8;
+    const int64_t cu = (int64_t)blockIdx.x * kWave + lane;   // 16-channel unit in the row
+    const int64_t col = cu * kLaneCh;
     const bool active = col < K;
     const int64_t cbase = (int64_t)blockIdx.x * kQChans;
 
@@ -220,39 +252,39 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
     // grid is sized to the number of workgroups the device holds at once),
     // and each wave issues the loads of its next batch before it processes
     // the current one, so loads stay in flight while the VALU works.
-    constexpr int RB = (LOWRANK || WF32 || RB4) ? 4 : 8;
+    constexpr int RB = WF32 ? 2 : 4;
     constexpr int WSTRIDE = kQThreads / kWave;    // waves per workgroup
-    const int64_t nrb = (M + rows_per_block - 1) / rows_per_block;
+    constexpr int RPB = WSTRIDE * RB;             // rows per block
+    const int64_t nrb = (M + RPB - 1) / RPB;
     auto load_batch = [&](RawRow<WF32> (&dst)[RB], int64_t rb) __attribute__((always_inline)) {
-        const int64_t ob = rb * rows_per_block + wave;
+        const int64_t ob = rb * RPB + wave;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int64_t o = ob + (int64_t)WSTRIDE * r;
-            if (rb < nrb && active && o < M) {
-                load_row<WF32>(dst[r], W, o, ldw, col);
-            } else {
-                dst[r].a = u32x4{0u, 0u, 0u, 0u};
-                dst[r].b = u32x4{0u, 0u, 0u, 0u};
-            }
+            if (rb < nrb && active && o < M) load_row<WF32>(dst[r], W, o, ldw, col);
+            else zero_row<WF32>(dst[r]);
         }
     };
-    const int lds_ranks = rank < kQLdsRanks ? rank : kQLdsRanks;
-    if constexpr (LOWRANK) {
-        for (int idx = threadIdx.x; idx < lds_ranks * kQChans; idx += kQThreads) {
-            const int k = idx / kQChans, c = idx % kQChans;
-            sA[idx] = (cbase + c < K) ? A[(int64_t)k * K + cbase + c] : 0.0f;
-        }
-    }
 
-    // Per-channel scales of this lane's 8 channels, and 1/s by v_rcp_f32
+    // the first batch of rows is in flight during the set-up below
+    RawRow<WF32> cur[RB];
+    load_batch(cur, blockIdx.y);
+
+    // Per-channel scales of this lane's 16 channels, and 1/s by v_rcp_f32
     // (exactly 1 for s = 1) for the dequantized weight.
-    float sc[8], sinv[8];
+    float sc[kLaneCh], sinv[kLaneCh];
     if constexpr (SFUSE) {
         // lambda from the statistics' block sums (same order as
-        // ttq_awq_scales), then each of the strip's 512 scales once per
-        // workgroup.
+        // ttq_awq_scales), then each of the strip's 1024 scales once per
+        // workgroup; the loads of both are issued before either is used.
         __shared__ float ssc[kQChans];
         __shared__ double lam_s;
+        double ssqv[kQChans / kQThreads];
+#pragma unroll
+        for (int h = 0; h < kQChans / kQThreads; ++h) {
+            const int64_t j = cbase + threadIdx.x + h * kQThreads;
+            ssqv[h] = j < K ? qs.ssq[j] : 0.0;
+        }
         if (wave == 0) {
             const double tot = blocks_total(qs.bsum, (K + kBlockCh - 1) / kBlockCh, lane);
             if (lane == 0) lam_s = qs.lambda_rel * (tot / (double)K);
@@ -263,174 +295,117 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
         for (int h = 0; h < kQChans / kQThreads; ++h) {
             const int c = threadIdx.x + h * kQThreads;
             const int64_t j = cbase + c;
-            const float v = j < K ? awq_scale(qs.ssq[j], qs.tn, lam, qs.e) : 1.0f;
+            const float v = j < K ? awq_scale(ssqv[h], qs.tn, lam, qs.e) : 1.0f;
             ssc[c] = v;
             if (j < K && blockIdx.y == 0) qs.s_out[j] = v;
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sc[i] = ssc[lane * 8 + i];
+        for (int i = 0; i < kLaneCh; ++i) sc[i] = ssc[lane * kLaneCh + i];
     } else {
-        if constexpr (LOWRANK) __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sc[i] = 1.0f;
+        for (int i = 0; i < kLaneCh; ++i) sc[i] = 1.0f;
         if (s != nullptr && active) {
-            f32x4 a = *(const f32x4*)(s + col), b = *(const f32x4*)(s + col + 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { sc[i] = a[i]; sc[4 + i] = b[i]; }
+            for (int k = 0; k < 4; ++k) {
+                const f32x4 a = *(const f32x4*)(s + col + 4 * k);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[4 * k + i] = a[i];
+            }
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sinv[i] = __builtin_amdgcn_rcpf(sc[i]);
+    for (int i = 0; i < kLaneCh; ++i) sinv[i] = __builtin_amdgcn_rcpf(sc[i]);
 
     const int64_t words_per_row = K * BITS / 32;
     const int64_t groups_per_row = K / GROUP;
 
-    RawRow<WF32> cur[RB];
-    load_batch(cur, blockIdx.y);
     for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
         RawRow<WF32> nxt[RB];
         load_batch(nxt, rb + gridDim.y);
-        const int64_t ob = rb * rows_per_block + wave;
-        if constexpr (LOWRANK) {
-            // Residual of the batch's RB rows, rank-ordered fp64 sums per
-            // element: each A value is read from LDS and widened once per
-            // batch and used for all RB rows.
-            double acc[RB][8];
-            const float* Brow[RB];
+        const int64_t ob = rb * RPB + wave;
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                float wv[8];
-                unpack_row<WF32>(cur[r], wv);
+        for (int r = 0; r < RB; ++r) {
+            const int64_t o = ob + (int64_t)WSTRIDE * r;
+            if (o >= M) break;                    // wave-uniform
+            float wv[kLaneCh];
+            unpack_row<WF32>(cur[r], wv);
+            float v[kLaneCh];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[r][i] = (double)wv[i];
-                const int64_t o = ob + (int64_t)WSTRIDE * r;
-                Brow[r] = B + (o < M ? o : M - 1) * rank;
-            }
-            for (int k = 0; k < rank; ++k) {
-                double ad[8];
-                if (k < lds_ranks) {
-                    const f32x4* ak = (const f32x4*)(sA + k * kQChans + lane * 8);
-                    const f32x4 a0 = ak[0], a1 = ak[1];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        ad[i] = (double)a0[i];
-                        ad[4 + i] = (double)a1[i];
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) ad[i] = active ? (double)A[(int64_t)k * K + col + i] : 0.0;
-                }
-#pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    const double nb = -(double)Brow[r][k];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[r][i] = __builtin_fma(nb, ad[i], acc[r][i]);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int64_t o = ob + (int64_t)WSTRIDE * r;
-                if (o >= M) break;                // wave-uniform
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[r][i] * (double)sc[i]);
-                quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
-                                                codes, scale, zero, sinv, wq, K);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int64_t o = ob + (int64_t)WSTRIDE * r;
-                if (o >= M) break;                // wave-uniform
-                float wv[8];
-                unpack_row<WF32>(cur[r], wv);
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = wv[i] * sc[i];
-                quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row,
-                                                codes, scale, zero, sinv, wq, K);
-            }
+            for (int i = 0; i < kLaneCh; ++i) v[i] = wv[i] * sc[i];
+            quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row, codes,
+                                            scale, zero, sinv, wq, K);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) cur[r] = nxt[r];
     }
 }
 
+// Workgroups per row strip so that the row blocks split evenly over the
+// workgroups the device holds at once (each walks the same number of them).
+int64_t persistent_rows_grid(int64_t resident, int64_t strips, int64_t nrb) {
+    int64_t gy = (resident + strips - 1) / strips;
+    if (gy > nrb) gy = nrb;
+    if (gy > 65535) gy = 65535;
+    if (gy < 1) gy = 1;
+    const int64_t rounds = (nrb + gy - 1) / gy;
+    return (nrb + rounds - 1) / rounds;
+}
+
+int resident_workgroups(const void* kern, int threads, size_t lds, OccMemo& memo, int slot_index) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    std::atomic<int>* slot = (dev >= 0 && dev < kMaxDevices) ? &memo.resident[dev][slot_index] : nullptr;
+    int resident = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (resident < 1) {
+        int cus = 256, per_cu = 1;
+        if (dev >= 0) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        resident = cus * per_cu;
+        if (slot) slot->store(resident, std::memory_order_relaxed);
+    }
+    return resident;
+}
+
 template <int BITS, int GROUP>
-static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw,
-                            const float* s, const float* B, const float* A, int rank,
+static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw, const float* s,
                             uint32_t* codes, uint16_t* scale, uint16_t* zero, uint16_t* wq,
                             const QScaleSrc* qs, hipStream_t st, StageTimer tm) {
-    const bool lr = rank > 0;
-    // Rows per block: one batch per wave (4 waves x 8 rows for bf16, x 4 for
-    // fp32 or with low-rank factors).  Large bf16 weights (more than 2^25
-    // values) also take batches of 4 rows: measured faster there (the
-    // 14336 x 4096 layer 64.8 -> 54.4 us, 4096 x 14336 51.7 -> 50.4 us),
-    // slower on 4096 x 4096 (19.9 -> 22.4 us).
-    const bool rb4 = !lr && !wf32 && M * K > ((int64_t)1 << 25);
-    const int rows = (lr || wf32 || rb4) ? 16 : 32;
     const int64_t strips = (K + kQChans - 1) / kQChans;
-    const int64_t nrb = (M + rows - 1) / rows;
-    const size_t lds = lr ? (size_t)(rank < kQLdsRanks ? rank : kQLdsRanks) * kQChans * sizeof(float) : 0;
+    const int rpb = wf32 ? 8 : 16;                // rows per block: 4 waves x RB
+    const int64_t nrb = (M + rpb - 1) / rpb;
     const QScaleSrc q = qs ? *qs : QScaleSrc{};
-    // Persistent row loop: as many workgroups as the device holds at once.
-    // The residency of each kernel instantiation is memoized per device and
-    // per LDS size (0..32 staged ranks of A): a value the runtime derives
-    // from the code object, the same on every call, so the memo never
-    // changes a result.
-    const int lds_ranks = lr ? (rank < kQLdsRanks ? rank : kQLdsRanks) : 0;
-    auto grid_for = [&](const void* kern, OccMemo& memo) -> dim3 {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-        std::atomic<int>* slot = (dev >= 0 && dev < kMaxDevices) ? &memo.resident[dev][lds_ranks] : nullptr;
-        int resident = slot ? slot->load(std::memory_order_relaxed) : 0;
-        if (resident < 1) {
-            int cus = 256, per_cu = 1;
-            if (dev >= 0) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kQThreads, lds) != hipSuccess ||
-                per_cu < 1)
-                per_cu = 1;
-            resident = cus * per_cu;
-            if (slot) slot->store(resident, std::memory_order_relaxed);
-        }
-        int64_t gy = ((int64_t)resident + strips - 1) / strips;
-        if (gy > nrb) gy = nrb;
-        if (gy > 65535) gy = 65535;
-        return dim3((unsigned)strips, (unsigned)gy);
-    };
-#define TTQ_Q_LAUNCH(WF, LR, SF, R4)                                                                     \
-    do {                                                                                                 \
-        static OccMemo memo;                                                                             \
-        auto kern = k_quantize<BITS, GROUP, WF, LR, SF, R4>;                                             \
-        return launch_kernel(kern, grid_for((const void*)kern, memo), dim3(kQThreads), lds, st, tm.start, \
-                             tm.stop, W, M, K, ldw, s, B, A, rank, rows, codes, scale, zero, wq, q);     \
+    // Persistent row loop over as many workgroups as the device holds at
+    // once.  The residency of each kernel instantiation is memoized per
+    // device: a value the runtime derives from the code object, the same on
+    // every call, so the memo never changes a result.
+#define TTQ_Q_LAUNCH(WF, SF)                                                                               \
+    do {                                                                                                   \
+        static OccMemo memo;                                                                               \
+        auto kern = k_quantize<BITS, GROUP, WF, SF>;                                                       \
+        const int64_t gy = persistent_rows_grid(resident_workgroups((const void*)kern, kQThreads, 0, memo, 0), \
+                                                strips, nrb);                                              \
+        return launch_kernel(kern, dim3((unsigned)strips, (unsigned)gy), dim3(kQThreads), 0, st, tm.start, \
+                             tm.stop, W, M, K, ldw, s, codes, scale, zero, wq, q);                         \
     } while (0)
-#define TTQ_Q_LAUNCH2(WF, LR, R4) \
-    if (qs) TTQ_Q_LAUNCH(WF, LR, true, R4); else TTQ_Q_LAUNCH(WF, LR, false, R4)
     if (wf32) {
-        if (lr) { TTQ_Q_LAUNCH2(true, true, false); } else { TTQ_Q_LAUNCH2(true, false, false); }
+        if (qs) TTQ_Q_LAUNCH(true, true); else TTQ_Q_LAUNCH(true, false);
     } else {
-        if (lr) { TTQ_Q_LAUNCH2(false, true, false); }
-        else if (rb4) { TTQ_Q_LAUNCH2(false, false, true); }
-        else { TTQ_Q_LAUNCH2(false, false, false); }
+        if (qs) TTQ_Q_LAUNCH(false, true); else TTQ_Q_LAUNCH(false, false);
     }
-
-#undef TTQ_Q_LAUNCH2
 #undef TTQ_Q_LAUNCH
-    return hipGetLastError();
 }
 
 template <int BITS>
-static hipError_t launch_q2(int group, const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw,
-                            const float* s, const float* B, const float* A, int rank,
+static hipError_t launch_q2(int group, const void* W, bool wf32, int64_t M, int64_t K, int64_t ldw, const float* s,
                             uint32_t* codes, uint16_t* scale, uint16_t* zero, uint16_t* wq,
                             const QScaleSrc* qs, hipStream_t st, StageTimer tm) {
     switch (group) {
-        case 16: return launch_q3<BITS, 16>(W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 32: return launch_q3<BITS, 32>(W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 64: return launch_q3<BITS, 64>(W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 128: return launch_q3<BITS, 128>(W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
+        case 16: return launch_q3<BITS, 16>(W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 32: return launch_q3<BITS, 32>(W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 64: return launch_q3<BITS, 64>(W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 128: return launch_q3<BITS, 128>(W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
     }
     return hipErrorInvalidValue;
 }
@@ -439,11 +414,13 @@ hipError_t launch_quantize(const void* W, bool wf32, int64_t M, int64_t K, int64
                            const float* s, int bits, int group, const float* B, const float* A,
                            int rank, uint32_t* codes, uint16_t* scale, uint16_t* zero,
                            uint16_t* wq, hipStream_t st, const QScaleSrc* qs, StageTimer tm) {
+    if (rank > 0)
+        return launch_quantize_lr(W, wf32, M, K, ldw, s, bits, group, B, A, rank, codes, scale, zero, wq, st, qs, tm);
     switch (bits) {
-        case 2: return launch_q2<2>(group, W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 3: return launch_q2<3>(group, W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 4: return launch_q2<4>(group, W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
-        case 5: return launch_q2<5>(group, W, wf32, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, qs, st, tm);
+        case 2: return launch_q2<2>(group, W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 3: return launch_q2<3>(group, W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 4: return launch_q2<4>(group, W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
+        case 5: return launch_q2<5>(group, W, wf32, M, K, ldw, s, codes, scale, zero, wq, qs, st, tm);
     }
     return hipErrorInvalidValue;
 }

@@ -44,13 +44,22 @@ __device__ __forceinline__ double cblock_sum(const double* __restrict__ ssq, int
 // by wave_sum_fixed.  mean(c) = blocks_total / K.
 __device__ __forceinline__ double blocks_total(const double* bs, int64_t nb, int lane) {
     double t = 0.0;
+#pragma unroll 8
     for (int64_t i = lane; i < nb; i += 64) t += bs[i];
     return wave_sum_fixed(t);
 }
 
+// (c + lambda)^e in fp64, rounded once to fp32.  The exponents of the
+// default settings, e = alpha / p = 1/4 (alpha 0.5, p 2) and 1/2, are
+// evaluated by correctly rounded square roots (one-tenth of the cost of
+// pow; the fp32 result equals the correctly rounded power except within
+// ~1e-16 of an fp32 rounding boundary); other exponents by fp64 pow.
 __device__ __forceinline__ float awq_scale(double ssq_j, double tn, double lam, double e) {
     const double cl = ssq_j / tn + lam;
-    return cl == 0.0 ? 1.0f : (float)pow(cl, e);
+    if (cl == 0.0) return 1.0f;
+    if (e == 0.25) return (float)__builtin_sqrt(__builtin_sqrt(cl));
+    if (e == 0.5) return (float)__builtin_sqrt(cl);
+    return (float)pow(cl, e);
 }
 
 }  // namespace ttq

@@ -328,15 +328,18 @@ def test_largest_K(T):
     # for the shrinkage mean): statistics, fused scales, quantization and the
     # projection for one, two and eight tokens.
     say("largest K = 2^18")
+    # The state is checked against the oracle (codes band-aware), Y element-
+    # wise against the projection of the library's own state (the fp32 bound
+    # for T <= 2) and against the oracle at the 2e-3 bar: with 4M codes, an
+    # in-band code difference moves a few outputs by ~1e-4 relative.
     K, M = 1 << 18, 16
     for Tn in (1, 2, 8):
         wl, d = _inputs("c2", seed=50 + Tn, T=Tn, K=K, M=M)
         ref = oracle.linear(d["X"], "bf16", d["W"], "bf16", 4, 32, 0.5, 1e-2)
         Y, st = _run_linear(T, wl, d)
-        np.testing.assert_allclose(host(st["ssq"]), ref["ssq"], rtol=1e-12)
-        np.testing.assert_allclose(host(st["s"]), ref["s"], rtol=S_TOL)
-        tol = 2e-5 if Tn <= 4 else Y_TOL
-        assert rel_fro(host(Y), ref["Y"]) < tol
+        _check_linear_state(wl, d, st, ref)
+        _check_y_on_state(wl, d, Y, st)
+        assert rel_fro(host(Y), ref["Y"]) < Y_TOL
 
 
 @pytest.mark.parametrize("Tn", [8, 12, 16])
