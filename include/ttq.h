@@ -220,9 +220,12 @@ ttq_status ttq_lowrank_add(const void* X, int xt, int64_t T, int64_t K, int64_t 
  *   Q = orth(A_s omega^T);  q times: Q = orth(A_s orth(A_s^T Q));
  *   Q^T A_s = U~ S V^T;  B = Q U~_r S_r,  A = V_r^T diag(1/s),
  * so that B A approximates W and B (A X) acts on the raw input; feed them
- * to ttq_quantize_groups / ttq_linear with the same s.  orth() is CholQR2
- * in fp64; the passes over W run on the matrix cores with fp32 accuracy;
- * the small eigenproblem is a fp64 Jacobi iteration.
+ * to ttq_quantize_groups / ttq_linear with the same s.  orth() is a
+ * Cholesky QR with an fp64 Gram matrix; the inner orth of each power
+ * iteration is omitted (orth(A_s orth(A_s^T Q)) = orth(A_s A_s^T Q) exactly,
+ * the inner orth being a right product with an upper triangular matrix of
+ * positive diagonal); the passes over W run on the matrix cores with fp32
+ * accuracy; the small eigenproblem is a fp64 Jacobi iteration.
  *   W: [M][K] bf16 (wt; fp32 W returns TTQ_ERR_UNSUPPORTED), stride ldw,
  *   K a multiple of 32.  s: [K] fp32.  omega: [l][K] fp32, the caller's
  *   Gaussian test vectors (one per row), 1 <= rank <= l <= 32, l <= M, K.

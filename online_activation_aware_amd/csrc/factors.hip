@@ -11,384 +11,797 @@
 //   B = Q U~_r S_r,  A[k][j] = (P U~)[j][k] / S_k   (= V_r^T diag(1/s)).
 // Om (l x K, l <= 32) is the caller's Gaussian test matrix.
 //
-// The passes over W are skinny products on the matrix cores (the Z = X A^T
-// kernel of the low-rank term, with W or a bf16 transpose of W as X and the
-// fp32 l-column operand split into three bf16 terms).  orth() is CholQR2:
-// G = Y^T Y in fp64 (fixed-order reduction), G = R^T R, Y R^-1, twice.  The
-// l x l eigenproblem is a cyclic Jacobi iteration in fp64 on one wave.
+// orth(Y) = Y R^-1 with Y^T Y = R^T R: a Cholesky QR with the Gram matrix
+// accumulated in fp64 from the stored fp32 rows, which leaves Q orthonormal
+// to fp32 rounding.  The inner orth of each power iteration is left out:
+// orth(A_s^T Q) = A_s^T Q R^-1 with R upper triangular with a positive
+// diagonal, and orth(X R^-1) = orth(X) for such R, so
+// orth(A_s orth(A_s^T Q)) = orth(A_s A_s^T Q) exactly.
+//
+// Two launches per pass over W (one stream, no host synchronisation):
+//  * k_fpass: Yp = X OP^T on the matrix cores for X = W or Wt (a bf16
+//    transpose of W made once by k_transpose_bf16).  A workgroup owns 128
+//    rows and one K slice and writes the slice's partial product.  It loads
+//    its operand inputs first and its slice of X after them, then forms the
+//    operand in LDS while X is in flight: the test vectors times s for the
+//    first pass, s^2 o P for the passes over W after a pass over W^T, and
+//    Q = Y R^-1 (fp64) for the passes over W^T.  OP is rounded to fp32 and
+//    split into three bf16 terms hi + mid + lo (fp32 accuracy against the
+//    exact bf16 X).
+//  * k_fgram: adds the slice partials of 128 rows in slice order and, where
+//    a Gram matrix is needed, forms the fp64 Gram partial of those rows
+//    (of rs o Y); the last workgroup to finish adds the partials in block
+//    order and factors the sum (one wave: Cholesky and R^-1 in registers).
+// Then k_fjacobi solves the l x l eigenproblem C C^T by parallel cyclic
+// Jacobi in fp64 (2 x 2 blocks per thread, one barrier per round; a
+// separate wave computes each round's rotations during the previous round)
+// and forms the small transforms of B and A, which k_fform applies.
+// Every reduction has a fixed order: results are bitwise reproducible.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace ttq {
 
 constexpr int kFMaxL = 32;
-constexpr int kGramRows = 64;                     // rows per Gram partial
-constexpr int kGramStage = 64;                    // rows staged in LDS at a time
+constexpr int kPassWaves = 8;
+constexpr int kPassRows = 16 * kPassWaves;        // rows of X per pass workgroup
+constexpr int kPassMaxKS = 512;                   // K slice per pass workgroup
+constexpr int kGramRows = 128;                    // rows per Gram partial
+constexpr int kGramThreads = 256;
 
-// Wt[j][o] = W[o][j] for o < M, 0 for M <= o < ldt (64 x 64 tiles via LDS).
+static int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
+static int round4(int x) { return (x + 3) / 4 * 4; }
+
+// Wt[j][o] = W[o][j] for o < M, 0 for M <= o < ldt; 64 x 64 tiles, 16-byte
+// loads and stores, the transposition in LDS.  Block (0, 0) also clears the
+// two completion counters of the Gram launches.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ W, int64_t M, int64_t K,
-                                                        int64_t ldw, uint16_t* __restrict__ Wt, int64_t ldt) {
-    __shared__ uint16_t tile[64][66];
+                                                        int64_t ldw, uint16_t* __restrict__ Wt, int64_t ldt,
+                                                        int* __restrict__ cnt) {
+    __shared__ uint32_t tile[64][33];             // [o][j pair], 2 bf16 per word
     const int64_t o0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
-    for (int r = ty; r < 64; r += 4) {
-        const int64_t o = o0 + r, j = j0 + tx;
-        tile[r][tx] = (o < M && j < K) ? W[o * ldw + j] : (uint16_t)0;
-    }
-    __syncthreads();
-    for (int r = ty; r < 64; r += 4) {
-        const int64_t j = j0 + r, o = o0 + tx;
-        if (j < K && o < ldt) Wt[j * ldt + o] = tile[tx][r];
-    }
-}
-
-// out[i][j] = in[i][j] * s[j]   (l x K).
-__global__ __launch_bounds__(256) void k_scale_cols(const float* __restrict__ in, int l, int64_t K,
-                                                    const float* __restrict__ s, float* __restrict__ out) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)l * K) return;
-    out[idx] = in[idx] * s[idx % K];
-}
-
-// Gram partials: chunk c (rows 64 c .. 64 c + 63 of Y [N][l], each row scaled
-// by rs[n] if given) -> Gp[c][a][b] = sum_n y_na y_nb in fp64, rows in order
-// (staged through LDS).
-__global__ __launch_bounds__(1024) void k_gram_partial(const float* __restrict__ Y, int64_t N, int l,
-                                                       const float* __restrict__ rs, double* __restrict__ Gp) {
-    __shared__ double ys[kGramStage][kFMaxL];
-    const int a = threadIdx.x / kFMaxL, b = threadIdx.x % kFMaxL;
-    double acc = 0.0;
-    for (int st = 0; st < kGramRows; st += kGramStage) {
-        const int64_t n0 = (int64_t)blockIdx.x * kGramRows + st;
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kGramStage * l; idx += 1024) {
-            const int r = idx / l, c = idx % l;
-            const int64_t n = n0 + r;
-            double v = 0.0;
-            if (n < N) v = (double)Y[n * l + c] * (rs ? (double)rs[n] : 1.0);
-            ys[r][c] = v;
+    const int t = threadIdx.x;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t < 2) cnt[t] = 0;
+    const int64_t rows = min((int64_t)64, M - o0);
+    const rsrc_t rw = make_rsrc(W + o0 * ldw, ((rows - 1) * ldw + K) * 2);   // rows >= M read as 0
+    {
+        const int r = t >> 3, c8 = (t & 7) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rr = r + 32 * h;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (j0 + c8 < K)
+                v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rw, (int)((rr * ldw + j0 + c8) * 2), 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tile[rr][c8 / 2 + e] = v[e];
         }
-        __syncthreads();
-        if (a < l && b < l)
-            for (int r = 0; r < kGramStage; ++r) acc = __builtin_fma(ys[r][a], ys[r][b], acc);
     }
-    if (a < l && b < l) Gp[((int64_t)blockIdx.x * l + a) * l + b] = acc;
+    __syncthreads();
+    const int o8 = (t & 7) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int jr = (t >> 3) + 32 * h;
+        const int64_t j = j0 + jr;
+        if (j >= K || o0 + o8 >= ldt) continue;
+        u32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = tile[o8 + 2 * e][jr >> 1], b = tile[o8 + 2 * e + 1][jr >> 1];
+            const uint32_t lo = (jr & 1) ? (a >> 16) : (a & 0xFFFFu);
+            const uint32_t hi = (jr & 1) ? (b >> 16) : (b & 0xFFFFu);
+            out[e] = lo | (hi << 16);
+        }
+        *(u32x4*)(Wt + j * ldt + o0 + o8) = out;
+    }
 }
 
-// Sum of the chunk partials Gp[c] (l x l) by a 1024-thread block, into
-// out[a][b] (LDS, row stride kFMaxL + 1): four groups of 256 threads add the
-// chunks c = g, g + 4, ... (all loads independent), then the four group sums
-// are added in group order.  Fixed order: bitwise reproducible.
-__device__ void sum_partials(const double* __restrict__ Gp, int nchunks, int l, double (*part)[kFMaxL * kFMaxL],
-                             double (*out)[kFMaxL + 1]) {
-    const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
-    const int ne = l * l;
-    for (int e = t; e < ne; e += 256) {
+// hi + mid + lo bf16 split of two fp32 values (the remainder is below 2^-24
+// of each), as packed pairs.
+__device__ __forceinline__ void split3(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = pack_bf16x2(x0, x1);
+    const float r0 = x0 - bf16lo_to_f32(hi), r1 = x1 - bf16hi_to_f32(hi);
+    mid = pack_bf16x2(r0, r1);
+    lo = pack_bf16x2(r0 - bf16lo_to_f32(mid), r1 - bf16hi_to_f32(mid));
+}
+
+// 1/sqrt(x) in fp64: the hardware estimate refined by two Newton steps (to
+// fp64 rounding level).
+__device__ __forceinline__ double rsq_f64(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+    const double h = 0.5 * x;
+    double e = __builtin_fma(-h * y, y, 0.5);
+    y = __builtin_fma(y, e, y);
+    e = __builtin_fma(-h * y, y, 0.5);
+    return __builtin_fma(y, e, y);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const u32x2 u = __builtin_bit_cast(u32x2, x);
+    u32x2 r;
+    r[0] = (unsigned)__builtin_amdgcn_readlane((int)u[0], lane);
+    r[1] = (unsigned)__builtin_amdgcn_readlane((int)u[1], lane);
+    return __builtin_bit_cast(double, r);
+}
+
+// One wave: G = R^T R (R upper, right-looking Cholesky) and Rinv = R^-1,
+// fp64, in registers.  Lane a holds row a of the working matrix (G on entry,
+// zero outside [l][l]); at step k the pivot and row k come from lane k by
+// readlane, and lanes a > k subtract G[a][k] G[k][b] / G[k][k].  Row k of
+// lane k is final after step k: R[k][b] = row_k[b] / R_kk.  Lane j builds
+// row j of R^-1 alongside: Rinv[j][k] = (delta_jk - sum_{m < k} Rinv[j][m]
+// R[m][k]) / R_kk.  A pivot <= 0 (exactly dependent columns, e.g. a zero
+// weight) gives R_kk = 1 and R_kj = 0, so that column of Y R^-1 is the
+// (zero) residual.  Writes Rinv [l][l] (zero below the diagonal).
+__device__ __forceinline__ void chol_inverse_wave(const double (*g)[kFMaxL + 1], int l, double* __restrict__ Rinv) {
+    const int a = threadIdx.x & (kWave - 1);
+    double row[kFMaxL], z[kFMaxL];                // z[m] = Rinv[a][m] / R_mm
+#pragma unroll
+    for (int b = 0; b < kFMaxL; ++b) {
+        row[b] = a < kFMaxL ? g[a][b] : 0.0;
+        z[b] = 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kFMaxL; ++k) {
+        if (k >= l) continue;                     // uniform
+        const double d = readlane_f64(row[k], k);
+        const bool ok = d > 0.0;
+        const double ir = ok ? rsq_f64(d) : 1.0;  // 1 / R_kk
+        const double dv = ok ? ir : 0.0;          // R[k][b] = row_k[b] dv for b > k
+        // Rinv[a][k]: R[m][k] = row_m[k] dv_m, with dv_m folded into z[m].
+        double acc = a == k ? 1.0 : 0.0;
+#pragma unroll
+        for (int m = 0; m < k; ++m) acc = __builtin_fma(-z[m], readlane_f64(row[k], m), acc);
+        const double yk = acc * ir;
+        z[k] = yk * dv;
+        if (a < l) Rinv[a * l + k] = yk;
+        // Trailing update of rows a > k.
+        const double w = a > k ? row[k] * (dv * dv) : 0.0;
+#pragma unroll
+        for (int b = k + 1; b < kFMaxL; ++b)
+            if (b < l) row[b] = __builtin_fma(-w, readlane_f64(row[b], k), row[b]);
+    }
+}
+
+// Operand of a pass: OP[i][k] for the K slice [kb, kb + kn).
+//   Yprev == nullptr: OP[i][k] = om[i][k] * (cs ? cs[k] : 1)   (om [l][ldo]).
+//   otherwise:        OP[i][k] = (sum_{c <= i} rs_k Yprev[k][c] Rinv[c][i]) * cs_k
+//                     in fp64 (Rinv [l][l] upper triangular; Rinv == nullptr:
+//                     the identity), rows k >= Nprev zero (Yprev [Nprev][LS]).
+struct PassOp {
+    const float* om;
+    int64_t ldo;
+    const float* Yprev;
+    int64_t Nprev;
+    const double* Rinv;
+    const float* rs;
+    const float* cs;
+};
+
+// Skinny product on the matrix cores: Yp[y][n][i] = sum over the K slice y
+// of X[n][k] * OP[i][k], i < 16 RT (rows i >= l of OP are zero), stored with
+// row stride LS.  X bf16 [N][ldx].  Wave w owns rows n0 + 16 w .. + 15;
+// thread t forms operand column kb + t.
+template <int RT>
+__global__ __launch_bounds__(kPassWaves * kWave) void k_fpass(const uint16_t* __restrict__ X, int64_t N,
+                                                              int64_t ldx, int64_t K, PassOp po, int l, int LS,
+                                                              int64_t ks, float* __restrict__ Yp) {
+    constexpr int kSteps = kPassMaxKS / 32;
+    constexpr int kRow = kPassMaxKS / 2 + 4;      // words per plane row (16-byte pad)
+    static_assert(kPassMaxKS == kPassWaves * kWave && kFMaxL * kFMaxL <= 2 * kPassMaxKS, "one operand row per thread");
+    __shared__ uint32_t sop[3][16 * RT][kRow];
+    __shared__ double rt[kFMaxL][kFMaxL];         // Rinv transposed: rt[i][c] = Rinv[c][i]
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * kPassRows;
+    const int64_t kb = (int64_t)blockIdx.y * ks;
+    const int kn = (int)min(ks, K - kb);          // a multiple of 32
+    const int nsteps = kn / 32;
+    const int64_t rows = min((int64_t)kPassRows, N - n0);
+    const rsrc_t rx = make_rsrc(X + n0 * ldx, ((rows - 1) * ldx + K) * 2);   // rows >= N read as 0
+
+    // Operand inputs first: the X loads issued after them stay in flight
+    // while the operand is formed (loads complete in issue order).
+    const int g8 = kn / 8;
+    constexpr int kOmIt = (16 * RT * (kPassMaxKS / 8) + kPassWaves * kWave - 1) / (kPassWaves * kWave);
+    float om8[kOmIt][8];
+    const int64_t k = kb + tid;
+    const bool kin = po.Yprev != nullptr && tid < kn && k < po.Nprev;
+    f32x4 yv[kFMaxL / 4];
+    double gv[2] = {0.0, 0.0};                    // Rinv entries tid, tid + 512
+    double rsk = 1.0, sck = 1.0;
+    if (po.Yprev == nullptr) {
+#pragma unroll
+        for (int it = 0; it < kOmIt; ++it) {
+            const int idx = tid + it * kPassWaves * kWave;
+            const int i = idx / g8, c8 = (idx % g8) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) om8[it][e] = 0.f;
+            if (idx < 16 * RT * g8 && i < l) {
+                const float* src = po.om + (int64_t)i * po.ldo + kb + c8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) om8[it][e] = src[e];
+                if (po.cs != nullptr)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) om8[it][e] *= po.cs[kb + c8 + e];
+            }
+        }
+    } else {
+        if (po.Rinv != nullptr)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (tid + u * kPassWaves * kWave < l * l) gv[u] = po.Rinv[tid + u * kPassWaves * kWave];
+        if (kin) {
+            if (po.rs != nullptr) rsk = (double)po.rs[k];
+            if (po.cs != nullptr) sck = (double)po.cs[k];
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < kFMaxL; c4 += 4)
+            yv[c4 / 4] = (kin && c4 < LS) ? *(const f32x4*)(po.Yprev + k * LS + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    u32x4 xb[kSteps];
+    const int64_t xrow = (int64_t)(16 * wave + r16) * ldx + kb + 8 * q;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+        xb[s] = s < nsteps ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rx, (int)((xrow + 32 * s) * 2), 0, 0))
+                           : u32x4{0u, 0u, 0u, 0u};
+
+    if (po.Yprev == nullptr) {
+#pragma unroll
+        for (int it = 0; it < kOmIt; ++it) {
+            const int idx = tid + it * kPassWaves * kWave;
+            if (idx >= 16 * RT * g8) continue;
+            const int i = idx / g8, c8 = (idx % g8) * 8;
+            u32x4 hi, mid, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h0, m0, l0;
+                split3(om8[it][2 * e], om8[it][2 * e + 1], h0, m0, l0);
+                hi[e] = h0;
+                mid[e] = m0;
+                lo[e] = l0;
+            }
+            *(u32x4*)&sop[0][i][c8 / 2] = hi;
+            *(u32x4*)&sop[1][i][c8 / 2] = mid;
+            *(u32x4*)&sop[2][i][c8 / 2] = lo;
+        }
+    } else {
+        // Row k = kb + tid of this slice, all outputs; pairs of rows are
+        // packed into bf16 words by the even lane.
+        float o[16 * RT];
+        if (po.Rinv != nullptr) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = tid + u * kPassWaves * kWave;
+                if (e < l * l) rt[e % l][e / l] = gv[u];
+            }
+            __syncthreads();                      // rt ready
+            double y[kFMaxL];
+#pragma unroll
+            for (int c = 0; c < kFMaxL; ++c) y[c] = (double)yv[c / 4][c % 4] * rsk;
+#pragma unroll
+            for (int i = 0; i < 16 * RT; ++i) {
+                o[i] = 0.f;
+                if (i < l) {
+                    double acc = 0.0;
+#pragma unroll
+                    for (int c = 0; c <= i; ++c)
+                        if (c < l) acc = __builtin_fma(y[c], rt[i][c], acc);
+                    o[i] = (float)(acc * sck);
+                }
+            }
+        } else {
+            const double sc2 = rsk * sck;
+#pragma unroll
+            for (int i = 0; i < 16 * RT; ++i) o[i] = i < l ? (float)((double)yv[i / 4][i % 4] * sc2) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16 * RT; ++i) {
+            const float on = __shfl_xor(o[i], 1);
+            if ((tid & 1) == 0 && tid < kn) {
+                uint32_t hi, mid, lo;
+                split3(o[i], on, hi, mid, lo);
+                sop[0][i][tid >> 1] = hi;
+                sop[1][i][tid >> 1] = mid;
+                sop[2][i][tid >> 1] = lo;
+            }
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        if (s >= nsteps) continue;                // wave-uniform
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int w = 16 * s + 4 * q;
+            const u32x4 hi = *(const u32x4*)&sop[0][16 * rt + r16][w];
+            const u32x4 mid = *(const u32x4*)&sop[1][16 * rt + r16][w];
+            const u32x4 lo = *(const u32x4*)&sop[2][16 * rt + r16][w];
+            acc[rt] = mfma_16x16x32(hi, xb[s], acc[rt]);
+            acc[rt] = mfma_16x16x32(mid, xb[s], acc[rt]);
+            acc[rt] = mfma_16x16x32(lo, xb[s], acc[rt]);
+        }
+    }
+    // Lane holds OUT^T[16 rt + 4 q + i][n0 + 16 wave + r16], i = 0..3.
+    const int64_t n = n0 + 16 * wave + r16;
+    if (n < N) {
+        float* yo = Yp + ((int64_t)blockIdx.y * N + n) * LS;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            if (16 * rt + 4 * q < LS) *(f32x4*)(yo + 16 * rt + 4 * q) = acc[rt];
+    }
+}
+
+// Ysum[n] = sum of the S slice partials of row n (slice order) and the fp64
+// Gram partial of rows kGramRows c .. + kGramRows - 1 scaled by rs[n] if
+// given: Gp[c][a][b] = sum_n (rs_n y_na)(rs_n y_nb), rows in order.  The
+// last workgroup to finish adds the partials in block order into G [l][l]
+// and, if Rinv is given, factors it (chol_inverse_wave) into Rinv.  G ==
+// nullptr: the slice sum only.  cnt: a completion counter, zero on entry,
+// left zero.
+__global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict__ Yp, int S, int64_t N, int LS, int l,
+                                                        const float* __restrict__ rs, float* __restrict__ Ysum,
+                                                        double* __restrict__ Gp, double* __restrict__ G,
+                                                        double* __restrict__ Rinv, int* __restrict__ cnt) {
+    __shared__ double ys[kGramRows][kFMaxL + 2];
+    __shared__ double gs[kFMaxL][kFMaxL + 1];
+    __shared__ int last;
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * kGramRows;
+    const int g4 = LS / 4;
+    for (int idx = tid; idx < kGramRows * g4; idx += kGramThreads) {
+        const int r = idx / g4, c4 = (idx % g4) * 4;
+        const int64_t n = n0 + r;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        double sc = 0.0;
+        if (n < N) {
+            // Slices in order, eight loads in flight at a time.
+            v = *(const f32x4*)(Yp + n * LS + c4);
+            for (int y0 = 1; y0 < S; y0 += 8) {
+                f32x4 w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    w[u] = y0 + u < S ? *(const f32x4*)(Yp + ((int64_t)(y0 + u) * N + n) * LS + c4)
+                                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (y0 + u < S)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += w[u][e];
+            }
+            *(f32x4*)(Ysum + n * LS + c4) = v;
+            sc = rs != nullptr ? (double)rs[n] : 1.0;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ys[r][c4 + e] = (double)v[e] * sc;
+    }
+    if (G == nullptr) return;
+    __syncthreads();
+    // Thread: the 4 x 4 block (ba, bb) of G over rows part, part + 4, ...
+    // (part = tid % 4); the four parts are added by shuffles, (0 + 1) + (2 + 3).
+    const int64_t ne = (int64_t)l * l;
+    {
+        const int blk = tid >> 2, part = tid & 3;
+        const int ba = blk >> 3, bb = blk & 7;
+        const bool act = 4 * ba < l && 4 * bb < l;
+        double acc[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[u][w] = 0.0;
+        if (act) {
+#pragma unroll 4
+            for (int r = part; r < kGramRows; r += 4) {
+                double x[4], y[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    x[u] = ys[r][4 * ba + u];
+                    y[u] = ys[r][4 * bb + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) acc[u][w] = __builtin_fma(x[u], y[w], acc[u][w]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc[u][w] += __shfl_xor(acc[u][w], 1);
+                acc[u][w] += __shfl_xor(acc[u][w], 2);
+            }
+        if (act && part == 0) {
+            double* gp = Gp + (int64_t)blockIdx.x * ne;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    if (4 * ba + u < l && 4 * bb + w < l) gp[(4 * ba + u) * l + 4 * bb + w] = acc[u][w];
+        }
+    }
+    // Completion count: release of this block's partial, then acquire by the
+    // last block.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last = atomicAdd(cnt, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const int nch = (int)gridDim.x;
+    for (int e = tid; e < ne; e += kGramThreads) {
         double acc = 0.0;
-#pragma unroll 8
-        for (int c = grp; c < nchunks; c += 4) acc += Gp[(int64_t)c * ne + e];
-        part[grp][e] = acc;
+        for (int c0 = 0; c0 < nch; c0 += 32) {
+            double v[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v[u] = c0 + u < nch ? Gp[(int64_t)(c0 + u) * ne + e] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) acc += v[u];
+        }
+        G[e] = acc;
+        gs[e / l][e % l] = acc;
     }
+    if (tid == 0) *cnt = 0;
+    if (Rinv == nullptr) return;
+    for (int e = tid; e < kFMaxL * kFMaxL; e += kGramThreads)
+        if (e / kFMaxL >= l || e % kFMaxL >= l) gs[e / kFMaxL][e % kFMaxL] = 0.0;
     __syncthreads();
-    for (int e = threadIdx.x; e < ne; e += 1024)
-        out[e / l][e % l] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
-    __syncthreads();
+    if (tid < kWave) chol_inverse_wave(gs, l, Rinv);
 }
 
-// G[a][b] = sum of the chunk partials.
-__global__ __launch_bounds__(1024) void k_gram_reduce(const double* __restrict__ Gp, int nchunks, int l,
-                                                      double* __restrict__ G) {
-    __shared__ double part[4][kFMaxL * kFMaxL];
-    __shared__ double g[kFMaxL][kFMaxL + 1];
-    sum_partials(Gp, nchunks, l, part, g);
-    for (int e = threadIdx.x; e < l * l; e += 1024) G[e] = g[e / l][e % l];
+// Rotation that zeroes a_pq (p < q): J[p][p] = J[q][q] = c, J[p][q] = s,
+// J[q][p] = -s with t = sgn(d) e / (|d| + r), d = a_qq - a_pp, e = 2 a_pq,
+// r = sqrt(d^2 + e^2), c = 1/sqrt(1 + t^2), s = t c (Golub and Van Loan,
+// Matrix Computations, the symmetric Schur decomposition), evaluated as
+// c = sqrt(w), w = (|d| + r) / (2 r), and s = sgn(d) e / (2 r sqrt(w)),
+// which follow from 1 + t^2 = 2 r / (|d| + r): two reciprocal square roots.
+__device__ __forceinline__ void jacobi_cs(double app, double aqq, double apq, double& c, double& s) {
+    c = 1.0;
+    s = 0.0;
+    if (apq == 0.0) return;
+    const double d = aqq - app, e = 2.0 * apq;
+    const double h = __builtin_fma(d, d, e * e);
+    const double y = rsq_f64(h);                  // 1 / r
+    const double w = 0.5 * (__builtin_fabs(d) + h * y) * y;
+    const double z = rsq_f64(w);
+    c = w * z;
+    s = (d >= 0.0 ? 0.5 : -0.5) * e * y * z;
 }
 
-// One workgroup: G = sum of the partials (sum_partials); G = R^T R (R upper,
-// right-looking Cholesky, one thread per entry), written to Rout.  A pivot
-// <= 0 (exactly dependent columns, e.g. a zero weight) gives R_kk = 1 and
-// R_kj = 0, so that column of Y R^-1 is the (zero) residual; `bad` counts
-// such pivots (diagnostics only).
-__global__ __launch_bounds__(1024) void k_chol(const double* __restrict__ Gp, int nchunks, int l,
-                                               double* __restrict__ Rout, int* __restrict__ bad) {
-    __shared__ double part[4][kFMaxL * kFMaxL];
-    __shared__ double g[kFMaxL][kFMaxL + 1];
-    __shared__ int nbad;
-    const int a = threadIdx.x / kFMaxL, b = threadIdx.x % kFMaxL;
-    if (threadIdx.x == 0) nbad = 0;
-    const bool in = a < l && b < l;
-    sum_partials(Gp, nchunks, l, part, g);
-    for (int k = 0; k < l; ++k) {
-        const double d = g[k][k];
-        __syncthreads();
-        if (a == k && in && b >= k)
-            g[k][b] = d > 0.0 ? ((b == k) ? __builtin_sqrt(d) : g[k][b] / __builtin_sqrt(d)) : (b == k ? 1.0 : 0.0);
-        if (threadIdx.x == 0 && !(d > 0.0)) nbad += 1;
-        __syncthreads();
-        if (in && a > k && b >= a) g[a][b] -= g[k][a] * g[k][b];
-        __syncthreads();
+// Partner of index x in round r of the round-robin ordering of n = m + 1
+// indices (x paired with m when x == r, m with r, otherwise with
+// (2 r - x) mod m), or x itself when the partner is the padding index (>= l).
+__device__ __forceinline__ int jacobi_partner(int x, int r, int m, int l) {
+    int p;
+    if (x == m) p = r;
+    else if (x == r) p = m;
+    else {
+        p = 2 * r - x;
+        p = p < 0 ? p + m : (p >= m ? p - m : p);
     }
-    if (in) Rout[a * l + b] = b >= a ? g[a][b] : 0.0;
-    if (threadIdx.x == 0) *bad = nbad;
+    return p < l ? p : x;
 }
 
-// out = (rs o Y) R^-1 per row n of Y [N][l]: q R = y by forward substitution
-// (q_c = (y_c - sum_{k<c} q_k R_kc) / R_cc), in fp64, rounded to fp32.  A
-// group of 32 lanes owns one row (lane c computes q_c; the q_k it needs come
-// from lanes k < c by shuffles, in order).
-// mode 0: out [N][l].  mode 1: out [l][ldo] transposed, times cs[n] if given
-// (columns N <= n < ldo are zero).
-__global__ __launch_bounds__(256) void k_apply_r(const float* __restrict__ Y, int64_t N, int l,
-                                                 const float* __restrict__ rs, const double* __restrict__ R,
-                                                 int mode, const float* __restrict__ cs, float* __restrict__ out,
-                                                 int64_t ldo) {
-    __shared__ double rr[kFMaxL * kFMaxL];
-    for (int i = threadIdx.x; i < l * l; i += 256) rr[i] = R[i];
-    __syncthreads();
-    const int c = threadIdx.x & 31;
-    const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 32;
-    const int64_t lim = mode == 0 ? N : ldo;
-    if (n >= lim) return;                         // uniform over the 32 lanes of a row
-    if (n >= N) {                                 // padding columns of the transposed operand
-        if (c < l) out[c * ldo + n] = 0.f;
-        return;
-    }
-    const double y = c < l ? (double)Y[n * l + c] * (rs ? (double)rs[n] : 1.0) : 0.0;
-    double v = y, q = 0.0;
-    for (int k = 0; k < l; ++k) {
-        // q_k is final once lane k has subtracted the terms of lanes < k.
-        const double qk = __shfl(c == k ? v / rr[k * l + k] : 0.0, k, 32);
-        if (c == k) q = qk;
-        if (c > k) v = __builtin_fma(-qk, rr[k * l + c], v);
-    }
-    if (c < l) {
-        if (mode == 0) out[n * l + c] = (float)q;
-        else out[c * ldo + n] = (float)(q * ((cs != nullptr) ? (double)cs[n] : 1.0));
-    }
+// (J^T A J)[x][y] for the rotation of this round: column x of J is
+// c_x e_x + s_x e_{p_x}.
+__device__ __forceinline__ double jacobi_entry(const double (*a)[kFMaxL + 1], int x, int y, double cx, double sx,
+                                               int px, double cy, double sy, int py) {
+    const double t1 = __builtin_fma(sy, a[x][py], cy * a[x][y]);
+    const double t2 = __builtin_fma(sy, a[px][py], cy * a[px][y]);
+    return __builtin_fma(sx, t2, cx * t1);
 }
 
-// Symmetric l x l eigenproblem G [l][l] by cyclic Jacobi.  A sweep is l-1
-// rounds of l/2 disjoint rotations (round-robin pairing); in a round every
-// index i has a partner p_i and a pair (c_i, s_i) with column i of the
-// rotation J equal to c_i e_i + s_i e_{p_i}, so one thread per entry forms
-// (J^T G J)[i][j] and (V J)[i][j] from the previous round's values.
-// Output: eigenvalues descending as sigma = sqrt(max(ev, 0)) and the matching
-// eigenvectors as columns of U [l][l].
-__global__ __launch_bounds__(1024) void k_jacobi(const double* __restrict__ G, int l, double* __restrict__ sig,
-                                                 double* __restrict__ U) {
-    // Two copies of A and V: a round reads one and writes the other, so it
-    // needs two barriers (rotations known, new values written) instead of a
-    // third one before overwriting in place.
+// Symmetric l x l eigenproblem of G = C C^T by cyclic Jacobi: a sweep is
+// n - 1 rounds of n/2 disjoint rotations in round-robin order (n = l rounded
+// up to even; in round r pair t is (r, n - 1) for t = 0, else
+// ((r + t) mod (n - 1), (r - t) mod (n - 1)); an index paired with n - 1 >= l
+// is not rotated), tabulated once.  Each round forms A' = J^T A J and
+// V' = V J: thread (tr, tc) of the first group owns the 2 x 2 block of A at
+// the rows of pair tr and the columns of pair tc (the rotation mixes exactly
+// those), thread (tr, tc) of the second group the same block of V, both
+// reading the previous round's copy; meanwhile lanes t < n/2 of the last
+// wave form the three entries of the next round's pair t from the same copy
+// and its rotation, so a round needs one barrier.  Stops when the
+// off-diagonal mass is at the rounding level of the trace (at most 30
+// sweeps).  Then, with sigma_k = sqrt(max(ev, 0)) descending, U~ the
+// matching eigenvectors and Rinv = R^-1 of the last basis (Q = YM R^-1):
+//   TB = R^-1 U~_r diag(sigma_r),  TA = U~_r diag(1/sigma_r) (0 where
+//   sigma = 0), both [l][rank] fp64.
+// blockDim: 2 (n/2)^2 threads rounded up to whole waves, plus one wave.
+__global__ __launch_bounds__(640) void k_fjacobi(const double* __restrict__ G, const double* __restrict__ Rinv, int l,
+                                                 int rank, double* __restrict__ TB, double* __restrict__ TA) {
     __shared__ double a[2][kFMaxL][kFMaxL + 1];
     __shared__ double v[2][kFMaxL][kFMaxL + 1];
-    __shared__ double rc[kFMaxL], rs_[kFMaxL];
-    __shared__ int ptn[kFMaxL];
+    __shared__ double rc[2][kFMaxL], rsn[2][kFMaxL];
+    __shared__ int ptab[kFMaxL][kFMaxL / 2];      // pair t of round r: p | q << 8, p < q
+    __shared__ int xtab[kFMaxL][kFMaxL];          // partner of x in round r (x itself if padding)
     __shared__ double wsum[16];
     __shared__ int order[kFMaxL];
+    __shared__ double sg[kFMaxL];
     const int tid = threadIdx.x;
-    const int i = tid / l, j = tid % l;           // blockDim = l*l rounded up to whole waves
-    const bool in = tid < l * l;
-    const int n = l + (l & 1);                    // even count for the pairing (a dummy index if odd)
-    if (in) {
-        a[0][i][j] = G[i * l + j];
-        v[0][i][j] = (i == j) ? 1.0 : 0.0;
+    const int nt = (int)blockDim.x, nw = nt >> 6;
+    const bool pw = (tid >> 6) == nw - 1;         // the pair wave: the last one
+    const int pt = tid & (kWave - 1);
+    const int n = l + (l & 1), m = n - 1, np = n / 2, nb = np * np;
+    const bool ta = tid < nb, tv = tid >= nb && tid < 2 * nb;
+    const int bi = ta ? tid : tid - nb;
+    const int tr = bi / np, tc = bi % np;
+    for (int e = tid; e < l * l; e += nt) {
+        a[0][e / l][e % l] = G[e];
+        v[0][e / l][e % l] = (e / l == e % l) ? 1.0 : 0.0;
+    }
+    for (int e = tid; e < m * np; e += nt) {
+        const int r = e / np, t = e % np;
+        int p, q;
+        if (t == 0) { p = r; q = m; }
+        else { p = (r + t) % m; q = (r + m - t) % m; }
+        if (p > q) { const int x = p; p = q; q = x; }
+        ptab[r][t] = p | (q << 8);
+        xtab[r][p] = q < l ? q : p;
+        if (q < l) xtab[r][q] = p;
+    }
+    __syncthreads();
+    auto publish = [&](int buf, int p, int q, double c, double s) {
+        if (q < l) {
+            rc[buf][p] = c; rsn[buf][p] = -s;
+            rc[buf][q] = c; rsn[buf][q] = s;
+        } else {
+            rc[buf][p] = 1.0; rsn[buf][p] = 0.0;
+        }
+    };
+    if (pw && pt < np) {                          // round 0 rotations from G
+        const int pq = ptab[0][pt], p = pq & 255, q = pq >> 8;
+        double c = 1.0, s = 0.0;
+        if (q < l) jacobi_cs(a[0][p][p], a[0][q][q], a[0][p][q], c, s);
+        publish(0, p, q, c, s);
     }
     __syncthreads();
     int cur = 0;
     double scale = 0.0;
     for (int k = 0; k < l; ++k) scale += a[0][k][k];
     for (int sweep = 0; sweep < 30; ++sweep) {
-        // Off-diagonal mass, reduced over the block in a fixed order.
-        double o = (in && i != j) ? a[cur][i][j] * a[cur][i][j] : 0.0;
-        for (int m = 32; m >= 1; m >>= 1) o += __shfl_xor(o, m);
+        double o = 0.0;
+        for (int e = tid; e < l * l; e += nt)
+            if (e / l != e % l) o = __builtin_fma(a[cur][e / l][e % l], a[cur][e / l][e % l], o);
+        for (int msk = 32; msk >= 1; msk >>= 1) o += __shfl_xor(o, msk);
         if ((tid & 63) == 0) wsum[tid >> 6] = o;
         __syncthreads();
         double tot = 0.0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += wsum[w];
-        // Stop when the off-diagonal mass is at the rounding level of the
-        // largest eigenvalues (cyclic Jacobi converges quadratically).
-        if (!(tot > 1e-28 * scale * scale)) break;
-        for (int round = 0; round < n - 1; ++round) {
+        for (int w = 0; w < nw; ++w) tot += wsum[w];
+        // Every thread holds the same tot; readfirstlane makes the exit
+        // visibly uniform, so the round loop runs on scalar control flow.
+        if (!__builtin_amdgcn_readfirstlane(tot > 1e-28 * scale * scale ? 1 : 0)) break;
+        for (int r = 0; r < m; ++r) {
             const double (*ac)[kFMaxL + 1] = a[cur];
-            if (tid < n / 2) {
-                int p, q;
-                if (tid == 0) { p = n - 1; q = round % (n - 1); }
-                else { p = (round + tid) % (n - 1); q = (round + n - 1 - tid) % (n - 1); }
-                if (p > q) { const int t = p; p = q; q = t; }
-                double c = 1.0, sn = 0.0;
-                if (q < l && ac[p][q] != 0.0) {
-                    const double th = (ac[q][q] - ac[p][p]) / (2.0 * ac[p][q]);
-                    const double t = (th >= 0.0 ? 1.0 : -1.0) / (__builtin_fabs(th) + __builtin_sqrt(th * th + 1.0));
-                    c = 1.0 / __builtin_sqrt(t * t + 1.0);
-                    sn = t * c;
+            if (ta || tv) {
+                const int px = ptab[r][tr], py = ptab[r][tc];
+                const int x0 = px & 255, x1 = px >> 8, y0 = py & 255, y1 = py >> 8;
+                const bool xv = x1 < l, yv = y1 < l;
+                const int x1c = xv ? x1 : x0, y1c = yv ? y1 : y0;
+                const double cy0 = rc[cur][y0], sy0 = rsn[cur][y0];
+                const double cy1 = rc[cur][y1c], sy1 = yv ? rsn[cur][y1c] : 0.0;
+                if (ta) {
+                    const double cx0 = rc[cur][x0], sx0 = rsn[cur][x0];
+                    const double cx1 = rc[cur][x1c], sx1 = xv ? rsn[cur][x1c] : 0.0;
+                    const double a00 = ac[x0][y0], a01 = yv ? ac[x0][y1c] : 0.0;
+                    const double a10 = xv ? ac[x1c][y0] : 0.0, a11 = (xv && yv) ? ac[x1c][y1c] : 0.0;
+                    // Columns (A J), then rows (J^T (A J)).
+                    const double b00 = __builtin_fma(sy0, a01, cy0 * a00), b01 = __builtin_fma(sy1, a00, cy1 * a01);
+                    const double b10 = __builtin_fma(sy0, a11, cy0 * a10), b11 = __builtin_fma(sy1, a10, cy1 * a11);
+                    double (*an)[kFMaxL + 1] = a[cur ^ 1];
+                    an[x0][y0] = __builtin_fma(sx0, b10, cx0 * b00);
+                    if (yv) an[x0][y1] = __builtin_fma(sx0, b11, cx0 * b01);
+                    if (xv) an[x1][y0] = __builtin_fma(sx1, b00, cx1 * b10);
+                    if (xv && yv) an[x1][y1] = __builtin_fma(sx1, b01, cx1 * b11);
+                } else {
+                    // V J on rows x0, x1.
+                    const double (*vc)[kFMaxL + 1] = v[cur];
+                    double (*vn)[kFMaxL + 1] = v[cur ^ 1];
+                    const double v00 = vc[x0][y0], v01 = vc[x0][y1c];
+                    const double v10 = vc[x1c][y0], v11 = vc[x1c][y1c];
+                    vn[x0][y0] = __builtin_fma(sy0, v01, cy0 * v00);
+                    if (yv) vn[x0][y1] = __builtin_fma(sy1, v00, cy1 * v01);
+                    if (xv) {
+                        vn[x1][y0] = __builtin_fma(sy0, v11, cy0 * v10);
+                        if (yv) vn[x1][y1] = __builtin_fma(sy1, v10, cy1 * v11);
+                    }
                 }
-                // J[p][p] = c, J[q][p] = -s, J[p][q] = s, J[q][q] = c.
-                if (p < l) { ptn[p] = q < l ? q : p; rc[p] = c; rs_[p] = q < l ? -sn : 0.0; }
-                if (q < l) { ptn[q] = p; rc[q] = c; rs_[q] = sn; }
             }
-            __syncthreads();
-            if (in) {
-                const int pi = ptn[i], pj = ptn[j];
-                const double ci = rc[i], si = rs_[i], cj = rc[j], sj = rs_[j];
-                a[cur ^ 1][i][j] = ci * (cj * ac[i][j] + sj * ac[i][pj]) + si * (cj * ac[pi][j] + sj * ac[pi][pj]);
-                v[cur ^ 1][i][j] = cj * v[cur][i][j] + sj * v[cur][i][pj];
+            if (pw && pt < np) {                  // next round's rotation of pair pt
+                const int pq2 = ptab[r + 1 == m ? 0 : r + 1][pt], p = pq2 & 255, q = pq2 >> 8;
+                double c = 1.0, s = 0.0;
+                if (q < l) {
+                    const int pp = xtab[r][p], pq = xtab[r][q];
+                    const double cp = rc[cur][p], sp = rsn[cur][p], cq = rc[cur][q], sq = rsn[cur][q];
+                    jacobi_cs(jacobi_entry(ac, p, p, cp, sp, pp, cp, sp, pp),
+                              jacobi_entry(ac, q, q, cq, sq, pq, cq, sq, pq),
+                              jacobi_entry(ac, p, q, cp, sp, pp, cq, sq, pq), c, s);
+                }
+                publish(cur ^ 1, p, q, c, s);
             }
             __syncthreads();
             cur ^= 1;
         }
     }
-    // Sort by eigenvalue, descending (ties keep index order).
+    // Descending eigenvalue order (ties keep index order): rank of each index.
     const double (*af)[kFMaxL + 1] = a[cur];
-    if (tid == 0) {
-        for (int k = 0; k < l; ++k) order[k] = k;
+    if (tid < l) {
+        const double ev = af[tid][tid];
+        int rk = 0;
         for (int k = 0; k < l; ++k) {
-            int best = k;
-            for (int m = k + 1; m < l; ++m)
-                if (af[order[m]][order[m]] > af[order[best]][order[best]]) best = m;
-            const int t = order[k]; order[k] = order[best]; order[best] = t;
+            const double ek = af[k][k];
+            rk += (ek > ev || (ek == ev && k < tid)) ? 1 : 0;
         }
+        order[rk] = tid;
     }
     __syncthreads();
     if (tid < l) {
         const double ev = af[order[tid]][order[tid]];
-        sig[tid] = __builtin_sqrt(ev > 0.0 ? ev : 0.0);
+        sg[tid] = __builtin_sqrt(ev > 0.0 ? ev : 0.0);
     }
-    if (in) U[i * l + j] = v[cur][i][order[j]];
+    __syncthreads();
+    // U~[x][k] = v[x][order[k]].
+    for (int e = tid; e < l * rank; e += nt) {
+        const int x = e / rank, k = e % rank;
+        const double sk = sg[k];
+        double t = 0.0;
+        for (int y = x; y < l; ++y) t = __builtin_fma(Rinv[x * l + y], v[cur][y][order[k]], t);
+        TB[e] = t * sk;
+        TA[e] = sk > 0.0 ? v[cur][x][order[k]] / sk : 0.0;
+    }
 }
 
-static unsigned jacobi_threads(int l) { return (unsigned)((l * l + 63) / 64 * 64); }
-
-// B[o][k] = sig_k * sum_i Q[o][i] U[i][k]   (k < rank), one thread per entry.
-__global__ __launch_bounds__(256) void k_form_b(const float* __restrict__ Q, int64_t M, int l, int rank,
-                                                const double* __restrict__ U, const double* __restrict__ sig,
-                                                float* __restrict__ B) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= M * rank) return;
-    const int64_t o = idx / rank;
-    const int k = (int)(idx % rank);
-    double acc = 0.0;
-    for (int i = 0; i < l; ++i) acc = __builtin_fma((double)Q[o * l + i], U[i * l + k], acc);
-    B[idx] = (float)(acc * sig[k]);
-}
-
-// A[k][j] = (sum_i P[j][i] U[i][k]) / sig_k   (k < rank; P = W^T Q), one
-// thread per entry (consecutive threads: consecutive j).
-__global__ __launch_bounds__(256) void k_form_a(const float* __restrict__ P, int64_t K, int l, int rank,
-                                                const double* __restrict__ U, const double* __restrict__ sig,
-                                                float* __restrict__ A) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= K * rank) return;
-    const int k = (int)(idx / K);
-    const int64_t j = idx % K;
-    double acc = 0.0;
-    for (int i = 0; i < l; ++i) acc = __builtin_fma((double)P[j * l + i], U[i * l + k], acc);
-    A[idx] = sig[k] > 0.0 ? (float)(acc / sig[k]) : 0.0f;
+// Blocks [0, nbb): B[o][k] = sum_c YM[o][c] TB[c][k] (o < M); the blocks
+// after them: A[k][j] = sum_c P[j][c] TA[c][k] (j < K); k < rank, fp64 sums
+// rounded to fp32.  YM and P have row stride LS; a block stages its 64 rows
+// and the transform in LDS, and thread (r, g) forms outputs k = g, g + 4, ...
+// of row r.
+__global__ __launch_bounds__(256) void k_fform(const float* __restrict__ YM, int64_t M, const float* __restrict__ P,
+                                               int64_t K, int LS, int l, int rank, const double* __restrict__ TB,
+                                               const double* __restrict__ TA, float* __restrict__ B,
+                                               float* __restrict__ A, unsigned nbb) {
+    __shared__ float rows[64][kFMaxL + 1];
+    __shared__ double tr[kFMaxL][kFMaxL];
+    const int tid = threadIdx.x;
+    const bool isb = blockIdx.x < nbb;
+    const int64_t r0 = (int64_t)(isb ? blockIdx.x : blockIdx.x - nbb) * 64;
+    const int64_t nrow = isb ? M : K;
+    const float* src = isb ? YM : P;
+    const double* T = isb ? TB : TA;
+    for (int e = tid; e < l * rank; e += 256) tr[e / rank][e % rank] = T[e];
+    const int g4 = LS / 4;
+    for (int e = tid; e < 64 * g4; e += 256) {
+        const int r = e / g4, c4 = (e % g4) * 4;
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (r0 + r < nrow) x = *(const f32x4*)(src + (r0 + r) * LS + c4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rows[r][c4 + u] = x[u];
+    }
+    __syncthreads();
+    const int r = tid >> 2, g = tid & 3;
+    const int64_t row = r0 + r;
+    if (row >= nrow) return;
+    double x[kFMaxL];
+#pragma unroll
+    for (int c = 0; c < kFMaxL; ++c) x[c] = c < l ? (double)rows[r][c] : 0.0;
+    for (int k = g; k < rank; k += 4) {
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < kFMaxL; ++c)
+            if (c < l) acc = __builtin_fma(x[c], tr[c][k], acc);
+        if (isb) B[row * rank + k] = (float)acc;
+        else A[(int64_t)k * K + row] = (float)acc;
+    }
 }
 
 // ------------------------------------------------------------------ host
 
-static int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
+// K slices of a pass over N rows with reduction length K: slices of at most
+// kPassMaxKS channels, more (down to 64 channels) while the row blocks alone
+// leave most of the 256 compute units idle.
+static int64_t pass_slice(int64_t N, int64_t K) {
+    const int64_t rb = (N + kPassRows - 1) / kPassRows;
+    int64_t ks = kPassMaxKS;
+    while (ks > 64 && rb * ((K + ks - 1) / ks) < 256) ks /= 2;
+    return ks;
+}
+static int64_t pass_slices(int64_t N, int64_t K) {
+    const int64_t ks = pass_slice(N, K);
+    return (K + ks - 1) / ks;
+}
 
 FactorsLayout factors_layout(int64_t M, int64_t K, int l) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     FactorsLayout F{};
     const int64_t M32 = round32(M);
+    const int LS = round4(l);
     const int64_t N = M > K ? M : K;
-    const int64_t NP = M32 > K ? M32 : K;
+    const int64_t ypn = pass_slices(M, K) * M > pass_slices(K, M32) * K ? pass_slices(M, K) * M
+                                                                        : pass_slices(K, M32) * K;
     size_t off = 0;
     F.wt = off;    off += up((size_t)K * M32 * 2);
-    F.y = off;     off += up((size_t)N * l * 4);          // pass output [N][l]
-    F.q1 = off;    off += up((size_t)N * l * 4);          // first CholQR basis [N][l]
-    F.qrow = off;  off += up((size_t)M * l * 4);          // final Q [M][l]
-    F.op = off;    off += up((size_t)l * NP * 4);         // next pass operand [l][K or M32]
+    F.yp = off;    off += up((size_t)ypn * LS * 4);        // pass partials [S][N][LS]
+    F.ym = off;    off += up((size_t)M * LS * 4);          // summed W pass [M][LS]
+    F.yk = off;    off += up((size_t)K * LS * 4);          // summed W^T pass [K][LS]
     F.gp = off;    off += up((size_t)((N + kGramRows - 1) / kGramRows) * l * l * 8);
-    F.rinv = off;  off += up((size_t)l * l * 8);
-    F.g = off;     off += up((size_t)l * l * 8);
-    F.sig = off;   off += up((size_t)l * 8);
-    F.u = off;     off += up((size_t)l * l * 8);
-    F.bad = off;   off += up(sizeof(int) * 2);
+    F.rinv = off;  off += up((size_t)l * l * 8);           // R^-1 of the latest basis
+    F.g = off;     off += up((size_t)l * l * 8);           // the latest Gram matrix
+    F.tb = off;    off += up((size_t)l * l * 8);
+    F.ta = off;    off += up((size_t)l * l * 8);
+    F.cnt = off;   off += up(2 * sizeof(int));
     F.total = off;
     return F;
 }
 
-bool factors_supported(bool wf32, int64_t M, int64_t K, int l, int rank) {
+bool factors_supported(bool wf32, int64_t M, int64_t K, int64_t ldw, int l, int rank) {
+    const int64_t M32 = round32(M);
     return !wf32 && M > 0 && K > 0 && K % 32 == 0 && l >= 1 && l <= kFMaxL && rank >= 1 && rank <= l &&
-           l <= M && l <= K && (int64_t)16 * (round32(M) > K ? round32(M) : K) * 2 < ((int64_t)1 << 31);
+           l <= M && l <= K && ldw >= K && (int64_t)kPassRows * (ldw > M32 ? ldw : M32) * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, const float* s, const float* om,
                           int l, int q, int rank, float* B, float* A, char* ws, hipStream_t st) {
     const FactorsLayout F = factors_layout(M, K, l);
     const int64_t M32 = round32(M);
+    const int LS = round4(l);
     uint16_t* Wt = (uint16_t*)(ws + F.wt);
-    float* Y = (float*)(ws + F.y);
-    float* Q1 = (float*)(ws + F.q1);
-    float* Qrow = (float*)(ws + F.qrow);
-    float* op = (float*)(ws + F.op);
+    float* Yp = (float*)(ws + F.yp);
+    float* YM = (float*)(ws + F.ym);
+    float* YK = (float*)(ws + F.yk);
     double* Gp = (double*)(ws + F.gp);
-    double* Rm = (double*)(ws + F.rinv);
-    double* Gm = (double*)(ws + F.g);
-    double* sig = (double*)(ws + F.sig);
-    double* U = (double*)(ws + F.u);
-    int* bad = (int*)(ws + F.bad);
+    double* G = (double*)(ws + F.g);
+    double* Rinv = (double*)(ws + F.rinv);
+    double* TB = (double*)(ws + F.tb);
+    double* TA = (double*)(ws + F.ta);
+    int* cnt = (int*)(ws + F.cnt);
     hipError_t e;
 #define TTQ_F(call) if ((e = (call)) != hipSuccess) return e
     TTQ_F(launch_kernel(k_transpose_bf16, dim3((unsigned)((K + 63) / 64), (unsigned)((M32 + 63) / 64)), dim3(256), 0,
-                        st, nullptr, nullptr, W, M, K, ldw, Wt, M32));
-    // orth(rs o Y) for Y [N][l]; result in op (mode 1, [l][ldo], times cs) and,
-    // when qrow is given, also row-major there.
-    auto cholqr2 = [&](const float* Yin, int64_t N, const float* rs, const float* cs, int64_t ldo,
-                       float* qrow) -> hipError_t {
-        const unsigned nch = (unsigned)((N + kGramRows - 1) / kGramRows);
-        auto rows_grid = [](int64_t n) { return dim3((unsigned)((n * 32 + 255) / 256)); };
-        hipError_t r;
-        if ((r = launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, Yin, N, l, rs, Gp)))
-            return r;
-        if ((r = launch_kernel(k_chol, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
-                               Rm, bad)))
-            return r;
-        if ((r = launch_kernel(k_apply_r, rows_grid(N), dim3(256), 0, st, nullptr, nullptr, Yin, N, l, rs,
-                               (const double*)Rm, 0, (const float*)nullptr, Q1, (int64_t)0)))
-            return r;
-        if ((r = launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, (const float*)Q1, N,
-                               l, (const float*)nullptr, Gp)))
-            return r;
-        if ((r = launch_kernel(k_chol, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
-                               Rm, bad + 1)))
-            return r;
-        if (qrow != nullptr &&
-            (r = launch_kernel(k_apply_r, rows_grid(N), dim3(256), 0, st, nullptr, nullptr, (const float*)Q1, N, l,
-                               (const float*)nullptr, (const double*)Rm, 0, (const float*)nullptr, qrow,
-                               (int64_t)0)))
-            return r;
-        return launch_kernel(k_apply_r, rows_grid(ldo), dim3(256), 0, st, nullptr, nullptr, (const float*)Q1, N, l,
-                             (const float*)nullptr, (const double*)Rm, 1, cs, op, ldo);
+                        st, nullptr, nullptr, W, M, K, ldw, Wt, M32, cnt));
+    // Yp = slices of X OP^T (X: N rows, reduction length Kr); then the slice
+    // sum into Ysum and (gram) the Gram matrix of rs o Ysum into G, factored
+    // into Rinv when chol is set.
+    auto pass = [&](const uint16_t* X, int64_t N, int64_t ldx, int64_t Kr, const PassOp& po, float* Ysum,
+                    const float* rs, bool gram, bool chol) -> hipError_t {
+        const int64_t ks = pass_slice(N, Kr);
+        const int S = (int)((Kr + ks - 1) / ks);
+        const dim3 g((unsigned)((N + kPassRows - 1) / kPassRows), (unsigned)S);
+        hipError_t r = l <= 16 ? launch_kernel(k_fpass<1>, g, dim3(kPassWaves * kWave), 0, st, nullptr, nullptr, X,
+                                               N, ldx, Kr, po, l, LS, ks, Yp)
+                               : launch_kernel(k_fpass<2>, g, dim3(kPassWaves * kWave), 0, st, nullptr, nullptr, X,
+                                               N, ldx, Kr, po, l, LS, ks, Yp);
+        if (r != hipSuccess) return r;
+        return launch_kernel(k_fgram, dim3((unsigned)((N + kGramRows - 1) / kGramRows)), dim3(kGramThreads), 0, st,
+                             nullptr, nullptr, (const float*)Yp, S, N, LS, l, rs, Ysum, Gp, gram ? G : nullptr,
+                             chol ? Rinv : nullptr, cnt);
     };
-    // Y = W (Om diag(s))^T;  Q = orth(Y) as the [l][M32] operand of W^T Q.
-    TTQ_F(launch_kernel(k_scale_cols, dim3((unsigned)(((int64_t)l * K + 255) / 256)), dim3(256), 0, st, nullptr,
-                        nullptr, om, l, K, s, op));
-    TTQ_F(launch_lowrank_z(W, false, M, K, ldw, op, l, Y, st, {}));
-    TTQ_F(cholqr2(Y, M, nullptr, nullptr, M32, q == 0 ? Qrow : nullptr));
+    // Y = W (Om diag(s))^T;  Y^T Y = R^T R;  Q = Y R^-1.
+    TTQ_F(pass(W, M, ldw, K, PassOp{om, K, nullptr, 0, nullptr, nullptr, s}, YM, nullptr, true, true));
     for (int it = 0; it < q; ++it) {
-        // P = W^T Q; Z = orth(diag(s) P) as the operand (diag(s) Z)^T [l][K].
-        TTQ_F(launch_lowrank_z(Wt, false, K, M32, M32, op, l, Y, st, {}));
-        TTQ_F(cholqr2(Y, K, s, s, K, nullptr));
-        // Y = W (diag(s) Z);  Q = orth(Y).
-        TTQ_F(launch_lowrank_z(W, false, M, K, ldw, op, l, Y, st, {}));
-        TTQ_F(cholqr2(Y, M, nullptr, nullptr, M32, it == q - 1 ? Qrow : nullptr));
+        // P = W^T Q.  The inner orth is left out: orth(A_s^T Q) = A_s^T Q R^-1
+        // with R upper triangular with a positive diagonal, and
+        // orth(A_s A_s^T Q R^-1) = orth(A_s A_s^T Q).
+        TTQ_F(pass(Wt, K, M32, M32, PassOp{nullptr, 0, YM, M, Rinv, nullptr, nullptr}, YK, nullptr, false, false));
+        // Y = A_s (A_s^T Q) = W (s^2 o P);  Y^T Y = R^T R.
+        TTQ_F(pass(W, M, ldw, K, PassOp{nullptr, 0, YK, K, nullptr, s, s}, YM, nullptr, true, true));
     }
-    // P = W^T Q (in Y [K][l]); C C^T = Gram of diag(s) P; factors.
-    TTQ_F(launch_lowrank_z(Wt, false, K, M32, M32, op, l, Y, st, {}));
-    const unsigned nch = (unsigned)((K + kGramRows - 1) / kGramRows);
-    TTQ_F(launch_kernel(k_gram_partial, dim3(nch), dim3(1024), 0, st, nullptr, nullptr, (const float*)Y, K, l, s, Gp));
-    TTQ_F(launch_kernel(k_gram_reduce, dim3(1), dim3(1024), 0, st, nullptr, nullptr, (const double*)Gp, (int)nch, l,
-                        Gm));
-    TTQ_F(launch_kernel(k_jacobi, dim3(1), dim3(jacobi_threads(l)), 0, st, nullptr, nullptr, (const double*)Gm, l,
-                        sig, U));
-    TTQ_F(launch_kernel(k_form_b, dim3((unsigned)((M * rank + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
-                        (const float*)Qrow, M, l, rank, (const double*)U, (const double*)sig, B));
-    TTQ_F(launch_kernel(k_form_a, dim3((unsigned)((K * rank + 255) / 256)), dim3(256), 0, st, nullptr, nullptr,
-                        (const float*)Y, K, l, rank, (const double*)U, (const double*)sig, A));
+    // P = W^T Q;  G = C C^T = Gram of diag(s) P;  eigenproblem;  factors.
+    TTQ_F(pass(Wt, K, M32, M32, PassOp{nullptr, 0, YM, M, Rinv, nullptr, nullptr}, YK, s, true, false));
+    const int np = (l + 1) / 2;
+    const unsigned jt = (unsigned)((2 * np * np + 63) / 64 * 64 + kWave);
+    TTQ_F(launch_kernel(k_fjacobi, dim3(1), dim3(jt), 0, st, nullptr, nullptr, (const double*)G,
+                        (const double*)Rinv, l, rank, TB, TA));
+    const unsigned nbb = (unsigned)((M + 63) / 64);
+    TTQ_F(launch_kernel(k_fform, dim3(nbb + (unsigned)((K + 63) / 64)), dim3(256), 0, st, nullptr, nullptr,
+                        (const float*)YM, M, (const float*)YK, K, LS, l, rank, (const double*)TB, (const double*)TA,
+                        B, A, nbb));
 #undef TTQ_F
     return hipSuccess;
 }

@@ -120,10 +120,10 @@ hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_
 
 // Per-prompt low-rank factors (factors.hip): workspace regions and the call.
 struct FactorsLayout {
-    size_t wt, y, q1, qrow, op, gp, rinv, g, sig, u, bad, total;
+    size_t wt, yp, ym, yk, gp, rinv, g, tb, ta, cnt, total;
 };
 FactorsLayout factors_layout(int64_t M, int64_t K, int l);
-bool factors_supported(bool wf32, int64_t M, int64_t K, int l, int rank);
+bool factors_supported(bool wf32, int64_t M, int64_t K, int64_t ldw, int l, int rank);
 hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, const float* s, const float* om,
                           int l, int q, int rank, float* B, float* A, char* ws, hipStream_t st);
 

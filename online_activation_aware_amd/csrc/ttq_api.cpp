@@ -281,7 +281,7 @@ ttq_status ttq_lowrank_factors(const void* W, int wt, int64_t M, int64_t K, int6
     TTQ_REQUIRE(omega != nullptr && aligned(omega, 4), "omega: null or misaligned");
     TTQ_REQUIRE(B != nullptr && aligned(B, 4) && A != nullptr && aligned(A, 4), "B/A: null or misaligned");
     if (wt == TTQ_F32) return fail(TTQ_ERR_UNSUPPORTED, "per-prompt factors need a bf16 weight");
-    TTQ_REQUIRE(ttq::factors_supported(false, M, K, l, rank), "sizes exceed the factor kernels' addressing");
+    TTQ_REQUIRE(ttq::factors_supported(false, M, K, ldw, l, rank), "sizes exceed the factor kernels' addressing");
     if (ttq_status e = check_ws(ws, ws_bytes, ttq::factors_layout(M, K, l).total)) return e;
     return device_status(ttq::launch_factors((const uint16_t*)W, M, K, ldw, s, omega, l, q, rank, B, A, (char*)ws,
                                              as_stream(stream)),
