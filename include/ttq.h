@@ -153,23 +153,33 @@ ttq_status ttq_quantize_groups(const void* W, int wt, int64_t M, int64_t K, int6
  *   (yt), overwritten.  Y must not overlap any input.
  *   Execution paths: for T <= 4 with K a multiple of 128 (decode steps) the
  *   vector ALUs compute step * (sum code * x/s - zero * sum x/s) per group
- *   in fp32, with no bf16 rounding; for 5 <= T <= 128 with K a multiple of
- *   128 (at most 16384) the codes stream straight into registers and are
+ *   in fp32, with no bf16 rounding; for bf16 X with 5 <= T <= 16, 4-bit
+ *   codes, groups of 32, 64 or 128 and K a multiple of 128 the matrix cores
+ *   compute the same per-group sums with x * (1/s) rounded once to bf16
+ *   (formed in LDS by the same launch, with its 32-channel sums) and each
+ *   code taken exactly as the bf16 number 128 + code (K split over
+ *   workgroups of 64 rows: fp32 partials in ws, added in slice order by a
+ *   second kernel); otherwise, for 5 <= T <= 128 with K a multiple
+ *   of 128 (at most 16384) the codes stream straight into registers and are
  *   expanded there to the bf16 weights above; for bf16 X with T >= 192 and
  *   K a multiple of 64 the weight is dequantized once into ws (M*K bf16) and
  *   multiplied by a matrix-core GEMM; otherwise codes are dequantized tile
  *   by tile inside the GEMM kernel.  The last three see bitwise the same
  *   bf16 weights.
- *   For bf16 X with 12 <= T <= 16 the expansion runs split over K (each
- *   workgroup: 64 rows, one K slice; fp32 partials in ws, added in slice
- *   order by a second kernel).  The T >= 192 GEMM also runs as two K slices
- *   when its 128 x 256 output tiles number fewer than 192 and K >= 8192 (a
- *   multiple of 128): fp32 partial products in ws, then Y = P0 + P1.
- *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (the
- *   split partials, S*T*M*4 for S <= K/128 slices, when 12 <= T <= 16; M*K*2
- *   when T >= 192, plus 2*T*M'*4 with M' = M rounded up to 4 when the GEMM
- *   runs as two K slices; each part rounded up to 256; none otherwise); only
- *   read and written by the kernels this call enqueues.
+ *   For bf16 X with 12 <= T <= 16 (where the sums path does not apply) the
+ *   expansion runs split over K (each workgroup: 64 rows, one K slice; fp32
+ *   partials in ws, added in slice order by a second kernel).  The T >= 192
+ *   GEMM also runs as two K slices when its 128 x 256 output tiles number
+ *   fewer than 192 and K >= 8192 (a multiple of 128): fp32 partial products
+ *   in ws, then Y = P0 + P1.
+ *   ws: at least ttq_workspace_bytes(T, K, M, bits, group, 0) bytes (for
+ *   5 <= T <= 16 and K a multiple of 128: the larger of S*T*M*4 for the
+ *   S K slices of the sums path (whole 512-channel sets, at most 8 a slice,
+ *   S*ceil(M/64) about 256; none when S = 1) and, when T >= 12, the split
+ *   partials S'*T*M*4 for S' <= K/128 slices; M*K*2 when T >= 192, plus 2*T*M'*4 with M' = M
+ *   rounded up to 4 when the GEMM runs as two K slices; each part rounded up
+ *   to 256; none otherwise); only read and written by the kernels this call
+ *   enqueues.
  */
 ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx,
                      const float* s, const int32_t* codes, const uint16_t* scale_f16,

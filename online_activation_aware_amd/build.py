@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libttq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["stats.hip", "quantize.hip", "quantize_lr.hip", "qgemm.hip", "qgemv.hip", "gemm_bf16.hip", "lowrank.hip", "factors.hip",
+SOURCES = ["stats.hip", "quantize.hip", "quantize_lr.hip", "qgemm.hip", "qgemv.hip", "qgemv_gs.hip", "gemm_bf16.hip", "lowrank.hip", "factors.hip",
            "noalloc.hip", "ttq_api.cpp"]
 
 FLAGS = [

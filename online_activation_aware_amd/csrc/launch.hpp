@@ -93,6 +93,18 @@ struct QgemvBatch {
     int64_t x = 0, s = 0, codes = 0, sz = 0, y = 0;
 };
 bool qgemv_supported(int64_t T, int64_t K, int64_t ldx, bool xf32);
+// kGsMinT <= T <= 16, bf16 X, 4-bit codes, groups of 32/64/128, K a
+// multiple of 128: the group scale applied to sums on the matrix cores
+// (qgemv_gs.hip); x/s and its 32-channel sums are formed in LDS by the same
+// launch.  A workspace of qgemv_gs_ws_bytes(T, K, M) bytes (256-byte
+// aligned; zero when K is not split) holds the fp32 partials of K slices.
+constexpr int64_t kGsMinT = 5;
+bool qgemv_gs_eligible(int64_t T, int64_t K, int64_t M, int bits, int group, bool xf32, int64_t ldx);
+size_t qgemv_gs_ws_bytes(int64_t T, int64_t K, int64_t M);
+hipError_t launch_qgemv_gs(const void* X, bool xf32, int64_t T, int64_t K, int64_t ldx, const float* s,
+                           const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, int bits,
+                           int group, void* Y, bool yf32, int64_t ldy, void* ws, hipStream_t st,
+                           StageTimer tm = {});
 // kSkMinT <= T <= 16, bf16 X, K a multiple of 128: split-K variant with an
 // fp32 partial workspace P of qgemv_sk_ws_bytes(T, K, M) bytes.
 constexpr int64_t kSkMinT = 12;

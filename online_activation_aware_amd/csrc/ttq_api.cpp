@@ -114,8 +114,13 @@ ttq_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // Prompt-sized projections stage the dequantized weight (M x K bf16) in the
 // workspace; the size is requested whenever T allows that path.
 size_t ws_qgemm(int64_t T, int64_t K, int64_t M) {
-    // 12 <= T <= 16: fp32 partials of the split-K few-token projection.
-    if (T >= ttq::kSkMinT && T <= 16 && K % 128 == 0) return round_up(ttq::qgemv_sk_ws_bytes(T, K, M));
+    // 5 <= T <= 16: the fp32 partials of the K slices of the sums kernel
+    // (4-bit codes) or of the split-K few-token projection.
+    if (T >= ttq::kGsMinT && T <= 16 && K % 128 == 0) {
+        const size_t gs = round_up(ttq::qgemv_gs_ws_bytes(T, K, M));
+        const size_t sk = T >= ttq::kSkMinT ? round_up(ttq::qgemv_sk_ws_bytes(T, K, M)) : 0;
+        return gs > sk ? gs : sk;
+    }
     if (T < ttq::kDequantGemmMinT) return 0;
     return ttq::dequant_ws_bytes(M, K) + round_up(ttq::gemm_bf16_split_ws_bytes(T, K, M));
 }
@@ -244,9 +249,14 @@ ttq_status ttq_qgemm(const void* X, int xt, int64_t T, int64_t K, int64_t ldx, c
     if (ttq_status e = check_state(s, codes, scale_f16, zero_f16, true)) return e;
     const bool xf32 = xt == TTQ_F32;
     const bool dq = use_dequant_gemm(T, xf32, K, ldx);
-    const bool sk = ttq::qgemv_sk_eligible(T, K, ldx, xf32);
-    if (ttq_status e = check_ws(ws, ws_bytes, (dq || sk) ? ws_qgemm(T, K, M) : 0)) return e;
+    const bool gs = ttq::qgemv_gs_eligible(T, K, M, bits, group, xf32, ldx);
+    const bool sk = !gs && ttq::qgemv_sk_eligible(T, K, ldx, xf32);
+    if (ttq_status e = check_ws(ws, ws_bytes, (dq || sk || gs) ? ws_qgemm(T, K, M) : 0)) return e;
     hipStream_t st = as_stream(stream);
+    if (gs)
+        return device_status(ttq::launch_qgemv_gs(X, xf32, T, K, ldx, s, (const uint32_t*)codes, scale_f16, zero_f16,
+                                                  M, bits, group, Y, yt == TTQ_F32, ldy, ws, st),
+                             "ttq_qgemm launch");
     if (sk)
         return device_status(ttq::launch_qgemv_sk(X, xf32, T, K, ldx, s, (const uint32_t*)codes, scale_f16, zero_f16,
                                                   M, bits, group, Y, yt == TTQ_F32, ldy, (float*)ws, st),
@@ -410,7 +420,13 @@ static ttq_status linear_layer(const ttq_linear_args* a, const double* ssq, cons
                                  a->A, a->rank, (uint32_t*)codes, scale, zero, wq, st, &qs, timer(1)),
             "quantize"))
         return e;
-    if (ttq::qgemv_sk_eligible(a->T, a->K, a->ldx, xf32)) {
+    if (ttq::qgemv_gs_eligible(a->T, a->K, a->M, a->bits, a->group, xf32, a->ldx)) {
+        if (ttq_status e = device_status(
+                ttq::launch_qgemv_gs(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero, a->M,
+                                     a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, scratch, st, timer(2)),
+                "qgemv"))
+            return e;
+    } else if (ttq::qgemv_sk_eligible(a->T, a->K, a->ldx, xf32)) {
         if (ttq_status e = device_status(
                 ttq::launch_qgemv_sk(a->X, xf32, a->T, a->K, a->ldx, s, (const uint32_t*)codes, scale, zero, a->M,
                                      a->bits, a->group, a->Y, a->yt == TTQ_F32, a->ldy, (float*)scratch, st,

@@ -281,6 +281,26 @@ def test_qgemv_parity(T, Tn, bits, group):
         assert err < (Y_TOL if xdt == "bf16" else 1e-4), (xdt, err)
 
 
+@pytest.mark.parametrize("Tn", [5, 7, 16])
+@pytest.mark.parametrize("group,K,M", [(32, 1152, 200), (64, 1152, 203), (128, 2048, 77), (32, 18432, 33),
+                                       (64, 256, 8200), (32, 14336, 1000)])
+def test_qgemv_group_sums(T, Tn, group, K, M):
+    # 4-bit codes, 5 <= T <= 16, bf16 X: the group scale applied to sums on
+    # the matrix cores (x * (1/s) rounded once to bf16 in LDS, codes exact as
+    # 128 + code); fp32 X takes the per-weight expansion.  K = 1152: nine
+    # chunks, the last 512-channel set partial, three K slices; M = 203 / 77
+    # / 33 partial 64-row blocks; K = 18432, M = 33: 36 slices; K = 256,
+    # M = 8200: one slice (no partials), half a set; K = 14336, M = 1000: two
+    # sets (two waves) per slice, 14 slices.
+    say(f"qgemv group sums T={Tn} group={group} K={K} M={M}")
+    for xdt in ("bf16", "f32"):
+        key = "c1" if xdt == "f32" else "c2"
+        for ydt in ("f32", "bf16"):
+            got, ref = _qgemm_case(T, key, Tn, K, M, 4, group, xdt, ydt, seed=Tn + group)
+            tol = Y_TOL if ydt == "f32" else Y_TOL_BF16_OUT
+            assert rel_fro(got, ref) < tol, (xdt, ydt)
+
+
 @pytest.mark.parametrize("Tn", [1, 2, 3, 4])
 @pytest.mark.parametrize("bits,group,K", [(4, 32, 1152), (4, 32, 4224), (3, 16, 4224), (2, 64, 18432),
                                           (5, 128, 4224), (4, 16, 2048), (2, 128, 1152),
