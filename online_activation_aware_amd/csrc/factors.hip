@@ -31,7 +31,8 @@
 //  * k_fgram: adds the slice partials of 128 rows in slice order and, where
 //    a Gram matrix is needed, forms the fp64 Gram partial of those rows
 //    (of rs o Y); the last workgroup to finish adds the partials in block
-//    order and factors the sum (one wave: Cholesky and R^-1 in registers).
+//    order and factors the sum (one wave: Cholesky and R^-1 in registers,
+//    each step's pivot row and column of R exchanged through LDS).
 // Then k_fjacobi solves the l x l eigenproblem C C^T by parallel cyclic
 // Jacobi in fp64 (2 x 2 blocks per thread, one barrier per round; a
 // separate wave computes each round's rotations during the previous round)
@@ -117,50 +118,67 @@ __device__ __forceinline__ double rsq_f64(double x) {
     return __builtin_fma(y, e, y);
 }
 
-__device__ __forceinline__ double readlane_f64(double x, int lane) {
-    const u32x2 u = __builtin_bit_cast(u32x2, x);
-    u32x2 r;
-    r[0] = (unsigned)__builtin_amdgcn_readlane((int)u[0], lane);
-    r[1] = (unsigned)__builtin_amdgcn_readlane((int)u[1], lane);
-    return __builtin_bit_cast(double, r);
-}
-
 // One wave: G = R^T R (R upper, right-looking Cholesky) and Rinv = R^-1,
-// fp64, in registers.  Lane a holds row a of the working matrix (G on entry,
-// zero outside [l][l]); at step k the pivot and row k come from lane k by
-// readlane, and lanes a > k subtract G[a][k] G[k][b] / G[k][k].  Row k of
-// lane k is final after step k: R[k][b] = row_k[b] / R_kk.  Lane j builds
-// row j of R^-1 alongside: Rinv[j][k] = (delta_jk - sum_{m < k} Rinv[j][m]
-// R[m][k]) / R_kk.  A pivot <= 0 (exactly dependent columns, e.g. a zero
-// weight) gives R_kk = 1 and R_kj = 0, so that column of Y R^-1 is the
-// (zero) residual.  Writes Rinv [l][l] (zero below the diagonal).
-__device__ __forceinline__ void chol_inverse_wave(const double (*g)[kFMaxL + 1], int l, double* __restrict__ Rinv) {
+// fp64.  Lane a holds row a of the working matrix in registers (G on
+// entry, zero outside [l][l]).  Step k: lane k publishes its row, and every
+// lane a its column-k entry R[a][k] (final for a < k), in LDS; each lane
+// reads them back (the same addresses in every lane), forms
+//   Rinv[a][k] = (delta_ak - sum_{m < k} Rinv[a][m] R[m][k]) / R_kk
+// (the sum split over four accumulators, m mod 4, added (0 + 1) + (2 + 3))
+// and, for a > k, subtracts G[a][k] G[k][b] / G[k][k] from its row.  Row k
+// is final after step k: R[k][b] = row_k[b] / R_kk.  A pivot <= 0 (exactly
+// dependent columns, e.g. a zero weight) gives R_kk = 1 and R_kj = 0, so
+// that column of Y R^-1 is the (zero) residual.  pub: LDS scratch of
+// 2 * kFMaxL doubles.  Writes Rinv [l][l] (zero below the diagonal).
+__device__ __forceinline__ void chol_inverse_wave(const double (*g)[kFMaxL + 1], int l, double* __restrict__ pub,
+                                                  double* __restrict__ Rinv) {
     const int a = threadIdx.x & (kWave - 1);
-    double row[kFMaxL], z[kFMaxL];                // z[m] = Rinv[a][m] / R_mm
+    double row[kFMaxL], z[kFMaxL];                // z[m] = Rinv[a][m]
+    double dvself = 0.0;                          // 1 / R_aa (0 for a rejected pivot)
 #pragma unroll
     for (int b = 0; b < kFMaxL; ++b) {
         row[b] = a < kFMaxL ? g[a][b] : 0.0;
         z[b] = 0.0;
     }
+    double* rowk = pub;                           // [kFMaxL]
+    double* colk = pub + kFMaxL;                  // [kFMaxL]: R[m][k]
 #pragma unroll
     for (int k = 0; k < kFMaxL; ++k) {
         if (k >= l) continue;                     // uniform
-        const double d = readlane_f64(row[k], k);
+        if (a == k) {
+#pragma unroll
+            for (int b = 0; b < kFMaxL; b += 2) *(double2*)(rowk + b) = double2{row[b], row[b + 1]};
+        }
+        if (a < k) colk[a] = row[k] * dvself;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the writes above have landed
+        __builtin_amdgcn_wave_barrier();
+        double rk[kFMaxL];
+#pragma unroll
+        for (int b = 0; b < kFMaxL; b += 2) {
+            const double2 v = *(const double2*)(rowk + b);
+            rk[b] = v.x;
+            rk[b + 1] = v.y;
+        }
+        const double d = rk[k];
         const bool ok = d > 0.0;
         const double ir = ok ? rsq_f64(d) : 1.0;  // 1 / R_kk
         const double dv = ok ? ir : 0.0;          // R[k][b] = row_k[b] dv for b > k
-        // Rinv[a][k]: R[m][k] = row_m[k] dv_m, with dv_m folded into z[m].
-        double acc = a == k ? 1.0 : 0.0;
+        if (a == k) dvself = dv;
+        double a4[4] = {a == k ? 1.0 : 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int m = 0; m < k; ++m) acc = __builtin_fma(-z[m], readlane_f64(row[k], m), acc);
-        const double yk = acc * ir;
-        z[k] = yk * dv;
+        for (int m = 0; m < k; ++m) a4[m & 3] = __builtin_fma(-z[m], colk[m], a4[m & 3]);
+        const double yk = ((a4[0] + a4[1]) + (a4[2] + a4[3])) * ir;
+        z[k] = yk;
         if (a < l) Rinv[a * l + k] = yk;
         // Trailing update of rows a > k.
         const double w = a > k ? row[k] * (dv * dv) : 0.0;
 #pragma unroll
         for (int b = k + 1; b < kFMaxL; ++b)
-            if (b < l) row[b] = __builtin_fma(-w, readlane_f64(row[b], k), row[b]);
+            if (b < l) row[b] = __builtin_fma(-w, rk[b], row[b]);
+        // Every lane has read rowk / colk before the next step rewrites them.
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -352,6 +370,7 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
                                                         double* __restrict__ Rinv, int* __restrict__ cnt) {
     __shared__ double ys[kGramRows][kFMaxL + 2];
     __shared__ double gs[kFMaxL][kFMaxL + 1];
+    __shared__ double pub[2 * kFMaxL];
     __shared__ int last;
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * kGramRows;
@@ -427,14 +446,18 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
                     if (4 * ba + u < l && 4 * bb + w < l) gp[(4 * ba + u) * l + 4 * bb + w] = acc[u][w];
         }
     }
-    // Completion count: release of this block's partial, then acquire by the
-    // last block.
-    __threadfence();
+    // Completion count: one thread releases the block's partial (the barrier
+    // orders the other waves' stores before it) and, in the last block,
+    // acquires the others'.  A device-scope fence writes back (release) or
+    // invalidates (acquire) the XCD's L2, so it runs once per workgroup.
     __syncthreads();
-    if (tid == 0) last = atomicAdd(cnt, 1) == (int)gridDim.x - 1;
+    if (tid == 0) {
+        __threadfence();
+        last = atomicAdd(cnt, 1) == (int)gridDim.x - 1;
+        if (last) __threadfence();
+    }
     __syncthreads();
     if (!last) return;
-    __threadfence();
     const int nch = (int)gridDim.x;
     for (int e = tid; e < ne; e += kGramThreads) {
         double acc = 0.0;
@@ -453,7 +476,7 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
     for (int e = tid; e < kFMaxL * kFMaxL; e += kGramThreads)
         if (e / kFMaxL >= l || e % kFMaxL >= l) gs[e / kFMaxL][e % kFMaxL] = 0.0;
     __syncthreads();
-    if (tid < kWave) chol_inverse_wave(gs, l, Rinv);
+    if (tid < kWave) chol_inverse_wave(gs, l, pub, Rinv);
 }
 
 // Rotation that zeroes a_pq (p < q): J[p][p] = J[q][q] = c, J[p][q] = s,
