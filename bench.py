@@ -263,10 +263,24 @@ def bench_workload(wl, args, dev, with_cpu: bool) -> dict:
         ttq.ttq_linear(Xs[i % ncopy], Ws[i % ncopy], wl.bits, wl.group, wl.alpha, wl.lambda_rel,
                        B=B, A=A, Y=Y, ws=ws, state=st, stage_events=events)
 
+    # Clock settling before the warm-up: steps run back to back for
+    # --settle-ms of wall time (untimed, reported as "settle").  On a GPU that
+    # was idle the clocks take tens of milliseconds of sustained work to reach
+    # their steady level; a handful of warm-up steps alone leaves the first
+    # timed steps ~10% slow (c2: ~99 us/layer after 5 steps, ~90 once warm).
+    settle_steps = 0
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(16):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"settled ({settle_steps} steps, {settle_ms:.0f} ms), warmup done ({args.warmup} steps)")
 
     # Timed region: K steps back to back, each ttq_linear called from
     # Python, nothing else on the stream.
@@ -389,7 +403,8 @@ def bench_workload(wl, args, dev, with_cpu: bool) -> dict:
                       "w_dtype": wl.wdtype, "y_dtype": "f32",
                       "cache": f"{ncopy} rotating copies of X and W ({ncopy * per_copy / 2**20:.0f} MiB)"},
            "stages": breakdown, "decode": decode, "factors": factors, "cpu_baseline": cpu,
-           "projection_flops": flops, "projection_us": proj_us}
+           "projection_flops": flops, "projection_us": proj_us,
+           "settle": {"steps": settle_steps, "ms": round(settle_ms, 1)}}
     del Xs, Ws, X0, W0, st, ws, Y
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -400,9 +415,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # 200 warm-up steps (20-40 ms of work): after a shorter warm-up the GPU's
-    # clocks are still rising and the first timed steps run ~10% slower.
     ap.add_argument("--warmup", type=int, default=200)
+    # Untimed steps for this many ms of wall time before the warm-up steps of
+    # each workload, so that the clocks have settled whatever --warmup is.
+    ap.add_argument("--settle-ms", type=float, default=150.0)
     ap.add_argument("--workload", default="all",
                     help="all (default: c2 as the headline, then c1, c3, c4, c5) or one of c1..c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -461,7 +477,8 @@ def main(argv=None) -> int:
                           f"(hipExtLaunchKernel), averaged over {args.steps} instrumented steps"}
 
     def summary(r):
-        d = {"us_per_layer": r["us_per_layer"], "config": r["config"], "stages": r["stages"]}
+        d = {"us_per_layer": r["us_per_layer"], "config": r["config"], "stages": r["stages"],
+             "settle": r["settle"]}
         if r["decode"]:
             d["decode"] = r["decode"]
         if r["factors"]:
@@ -475,6 +492,8 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": dict(head["settle"], note="untimed steps run for --settle-ms of wall time before the "
+                       "warm-up steps, so the clocks have settled whatever --warmup is"),
         "ms_per_step": round(head["us_per_layer"] / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
