@@ -30,9 +30,10 @@
 //    exact bf16 X).
 //  * k_fgram: adds the slice partials of 128 rows in slice order and, where
 //    a Gram matrix is needed, forms the fp64 Gram partial of those rows
-//    (of rs o Y); the last workgroup to finish adds the partials in block
-//    order and factors the sum (one wave: Cholesky and R^-1 in registers,
-//    each step's pivot row and column of R exchanged through LDS).
+//    (of rs o Y); then k_fgram_sum (one workgroup) adds the partials in
+//    block order and factors the sum (one wave: Cholesky and R^-1 in
+//    registers, each step's pivot row and column of R exchanged through
+//    LDS).
 // Then k_fjacobi solves the l x l eigenproblem C C^T by parallel cyclic
 // Jacobi in fp64 (2 x 2 blocks per thread, one barrier per round; a
 // separate wave computes each round's rotations during the previous round)
@@ -55,15 +56,12 @@ static int64_t round32(int64_t x) { return (x + 31) / 32 * 32; }
 static int round4(int x) { return (x + 3) / 4 * 4; }
 
 // Wt[j][o] = W[o][j] for o < M, 0 for M <= o < ldt; 64 x 64 tiles, 16-byte
-// loads and stores, the transposition in LDS.  Block (0, 0) also clears the
-// two completion counters of the Gram launches.
+// loads and stores, the transposition in LDS.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ W, int64_t M, int64_t K,
-                                                        int64_t ldw, uint16_t* __restrict__ Wt, int64_t ldt,
-                                                        int* __restrict__ cnt) {
+                                                        int64_t ldw, uint16_t* __restrict__ Wt, int64_t ldt) {
     __shared__ uint32_t tile[64][33];             // [o][j pair], 2 bf16 per word
     const int64_t o0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
     const int t = threadIdx.x;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && t < 2) cnt[t] = 0;
     const int64_t rows = min((int64_t)64, M - o0);
     const rsrc_t rw = make_rsrc(W + o0 * ldw, ((rows - 1) * ldw + K) * 2);   // rows >= M read as 0
     {
@@ -359,19 +357,12 @@ __global__ __launch_bounds__(kPassWaves * kWave) void k_fpass(const uint16_t* __
 
 // Ysum[n] = sum of the S slice partials of row n (slice order) and the fp64
 // Gram partial of rows kGramRows c .. + kGramRows - 1 scaled by rs[n] if
-// given: Gp[c][a][b] = sum_n (rs_n y_na)(rs_n y_nb), rows in order.  The
-// last workgroup to finish adds the partials in block order into G [l][l]
-// and, if Rinv is given, factors it (chol_inverse_wave) into Rinv.  G ==
-// nullptr: the slice sum only.  cnt: a completion counter, zero on entry,
-// left zero.
+// given: Gp[c][a][b] = sum_n (rs_n y_na)(rs_n y_nb), rows in order
+// (k_fgram_sum adds them).  Gp == nullptr: the slice sum only.
 __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict__ Yp, int S, int64_t N, int LS, int l,
                                                         const float* __restrict__ rs, float* __restrict__ Ysum,
-                                                        double* __restrict__ Gp, double* __restrict__ G,
-                                                        double* __restrict__ Rinv, int* __restrict__ cnt) {
+                                                        double* __restrict__ Gp) {
     __shared__ double ys[kGramRows][kFMaxL + 2];
-    __shared__ double gs[kFMaxL][kFMaxL + 1];
-    __shared__ double pub[2 * kFMaxL];
-    __shared__ int last;
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * kGramRows;
     const int g4 = LS / 4;
@@ -401,7 +392,7 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
 #pragma unroll
         for (int e = 0; e < 4; ++e) ys[r][c4 + e] = (double)v[e] * sc;
     }
-    if (G == nullptr) return;
+    if (Gp == nullptr) return;
     __syncthreads();
     // Thread: the 4 x 4 block (ba, bb) of G over rows part, part + 4, ...
     // (part = tid % 4); the four parts are added by shuffles, (0 + 1) + (2 + 3).
@@ -446,19 +437,18 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
                     if (4 * ba + u < l && 4 * bb + w < l) gp[(4 * ba + u) * l + 4 * bb + w] = acc[u][w];
         }
     }
-    // Completion count: one thread releases the block's partial (the barrier
-    // orders the other waves' stores before it) and, in the last block,
-    // acquires the others'.  A device-scope fence writes back (release) or
-    // invalidates (acquire) the XCD's L2, so it runs once per workgroup.
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(cnt, 1) == (int)gridDim.x - 1;
-        if (last) __threadfence();
-    }
-    __syncthreads();
-    if (!last) return;
-    const int nch = (int)gridDim.x;
+}
+
+// G = sum of the nch Gram partials in block order (one workgroup; a second
+// launch after k_fgram instead of a completion count, since a device-scope
+// fence in every k_fgram workgroup writes back and invalidates its XCD's L2)
+// and, if Rinv is given, its Cholesky factor's inverse (chol_inverse_wave).
+__global__ __launch_bounds__(kGramThreads) void k_fgram_sum(const double* __restrict__ Gp, int nch, int l,
+                                                            double* __restrict__ G, double* __restrict__ Rinv) {
+    __shared__ double gs[kFMaxL][kFMaxL + 1];
+    __shared__ double pub[2 * kFMaxL];
+    const int tid = threadIdx.x;
+    const int64_t ne = (int64_t)l * l;
     for (int e = tid; e < ne; e += kGramThreads) {
         double acc = 0.0;
         for (int c0 = 0; c0 < nch; c0 += 32) {
@@ -471,7 +461,6 @@ __global__ __launch_bounds__(kGramThreads) void k_fgram(const float* __restrict_
         G[e] = acc;
         gs[e / l][e % l] = acc;
     }
-    if (tid == 0) *cnt = 0;
     if (Rinv == nullptr) return;
     for (int e = tid; e < kFMaxL * kFMaxL; e += kGramThreads)
         if (e / kFMaxL >= l || e % kFMaxL >= l) gs[e / kFMaxL][e % kFMaxL] = 0.0;
@@ -758,7 +747,6 @@ FactorsLayout factors_layout(int64_t M, int64_t K, int l) {
     F.g = off;     off += up((size_t)l * l * 8);           // the latest Gram matrix
     F.tb = off;    off += up((size_t)l * l * 8);
     F.ta = off;    off += up((size_t)l * l * 8);
-    F.cnt = off;   off += up(2 * sizeof(int));
     F.total = off;
     return F;
 }
@@ -783,11 +771,10 @@ hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, 
     double* Rinv = (double*)(ws + F.rinv);
     double* TB = (double*)(ws + F.tb);
     double* TA = (double*)(ws + F.ta);
-    int* cnt = (int*)(ws + F.cnt);
     hipError_t e;
 #define TTQ_F(call) if ((e = (call)) != hipSuccess) return e
     TTQ_F(launch_kernel(k_transpose_bf16, dim3((unsigned)((K + 63) / 64), (unsigned)((M32 + 63) / 64)), dim3(256), 0,
-                        st, nullptr, nullptr, W, M, K, ldw, Wt, M32, cnt));
+                        st, nullptr, nullptr, W, M, K, ldw, Wt, M32));
     // Yp = slices of X OP^T (X: N rows, reduction length Kr); then the slice
     // sum into Ysum and (gram) the Gram matrix of rs o Ysum into G, factored
     // into Rinv when chol is set.
@@ -801,9 +788,12 @@ hipError_t launch_factors(const uint16_t* W, int64_t M, int64_t K, int64_t ldw, 
                                : launch_kernel(k_fpass<2>, g, dim3(kPassWaves * kWave), 0, st, nullptr, nullptr, X,
                                                N, ldx, Kr, po, l, LS, ks, Yp);
         if (r != hipSuccess) return r;
-        return launch_kernel(k_fgram, dim3((unsigned)((N + kGramRows - 1) / kGramRows)), dim3(kGramThreads), 0, st,
-                             nullptr, nullptr, (const float*)Yp, S, N, LS, l, rs, Ysum, Gp, gram ? G : nullptr,
-                             chol ? Rinv : nullptr, cnt);
+        const unsigned nch = (unsigned)((N + kGramRows - 1) / kGramRows);
+        r = launch_kernel(k_fgram, dim3(nch), dim3(kGramThreads), 0, st, nullptr, nullptr, (const float*)Yp, S, N,
+                          LS, l, rs, Ysum, gram ? Gp : nullptr);
+        if (r != hipSuccess || !gram) return r;
+        return launch_kernel(k_fgram_sum, dim3(1), dim3(kGramThreads), 0, st, nullptr, nullptr, (const double*)Gp,
+                             (int)nch, l, G, chol ? Rinv : nullptr);
     };
     // Y = W (Om diag(s))^T;  Y^T Y = R^T R;  Q = Y R^-1.
     TTQ_F(pass(W, M, ldw, K, PassOp{om, K, nullptr, 0, nullptr, nullptr, s}, YM, nullptr, true, true));

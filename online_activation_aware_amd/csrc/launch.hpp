@@ -132,7 +132,7 @@ hipError_t launch_lowrank(const void* X, bool xf32, int64_t T, int64_t K, int64_
 
 // Per-prompt low-rank factors (factors.hip): workspace regions and the call.
 struct FactorsLayout {
-    size_t wt, yp, ym, yk, gp, rinv, g, tb, ta, cnt, total;
+    size_t wt, yp, ym, yk, gp, rinv, g, tb, ta, total;
 };
 FactorsLayout factors_layout(int64_t M, int64_t K, int l);
 bool factors_supported(bool wf32, int64_t M, int64_t K, int64_t ldw, int l, int rank);

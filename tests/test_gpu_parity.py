@@ -258,6 +258,16 @@ def test_qgemm_ragged_and_bf16_output(T, Tn, M):
         assert rel_fro(got, ref) < tol
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 448])
+def test_qgemm_short_k_wide_tiles(T, K):
+    # 128 x 256 projection tiles (6144 rows x 1000 tokens: 192 tiles, the
+    # last token tile ragged) with 1 to 7 K steps of 64: fewer steps than
+    # the W~ ring has slots, and every remainder of the three-step unroll.
+    say(f"qgemm short K={K}, 128x256 tiles")
+    got, ref = _qgemm_case(T, "c2", 1000, K, 6144, 4, 32, "bf16", "f32", seed=K)
+    assert rel_fro(got, ref) < Y_TOL
+
+
 @pytest.mark.parametrize("Tn,M", [(300, 130), (600, 1024)])
 def test_qgemm_split_k(T, Tn, M):
     # ttq_qgemm at prompt-sized T with few output tiles and K = 8192: the
