@@ -279,109 +279,46 @@ __global__ __launch_bounds__(vwaves(NT) * kWave) void k_qgemv(
 // formed once per wave in fp32 (x * v_rcp(s)), so the only rounding is fp32
 // accumulation: no bf16 rounding of weights or tokens on this path.
 //
-// Mapping: a piece is 64 lanes x LC consecutive channels (LC = 32: 2048
-// channels, b x 256 bytes of codes per row; LC = 16 for one token at even b:
-// 1024 channels, so twice the waves stream the same bytes and the waves of a
-// SIMD cover each other's waits: 14336 -> 4096, T = 1: 11.15 -> 10.76 us).
-// A group spanning several lanes is mapped on each lane's part of its sums.
-// A workgroup owns RW rows; its NS waves take the pieces w, w + NS, ...;
-// per piece a wave issues the codes of all RW rows (one contiguous load of
-// LC b / 8 bytes per lane and row) before it computes, so each load
-// instruction reads a contiguous run of one row.  Per-lane sums are added
-// over the wave by a fixed butterfly and over the waves in wave order
-// (deterministic).
-constexpr int tpiece(int lc) { return lc * kWave; }   // channels per piece
-constexpr int tmaxwaves(int lc) { return lc == 32 ? 8 : 16; }
-constexpr int kTMaxWaves = 16;
+// Mapping: a piece is 64 lanes x 32 consecutive channels (2048 channels;
+// b x 256 bytes of codes per row).  A workgroup owns RW rows; its NS waves
+// take the pieces w, w + NS, ...; per piece a wave issues the codes of all
+// RW rows (one contiguous 16-byte load per lane and row at b = 4) before it
+// computes, so each load instruction reads a contiguous b x 256-byte run of
+// one row.  Per-lane sums are added over the wave by a fixed butterfly and
+// over the waves in wave order (deterministic).
+constexpr int kTPiece = kTChan * kWave;           // channels per piece
+constexpr int kTMaxWaves = 8;
 // 16 rows per workgroup: the grid's waves fit the chip in one round.  Rows
 // in flight per wave: 3 for one token, 2 for two, 1 for four (registers).
 constexpr int trows(int tt) { return 16; }
 constexpr int tdepth(int tt) { return tt == 1 ? 3 : tt == 2 ? 2 : 1; }
 
-// The codes of an LC-channel field: BITS words (32 channels) or BITS / 2
-// (16 channels, even BITS).
-template <int BITS, int LC>
-struct FieldWords {
-    static constexpr int NW = LC * BITS / 32;
-    uint32_t w[NW];
-};
-
-template <int BITS, int LC>
-__device__ __forceinline__ void load_field(FieldWords<BITS, LC>& f, const uint32_t* __restrict__ p) {
-    if constexpr (LC == 32) {
-        CodeWords<BITS> c;
-        load_codes<BITS>(c, p);
-#pragma unroll
-        for (int i = 0; i < BITS; ++i) f.w[i] = c.w[i];
-    } else if constexpr (BITS == 4) {
-        const u32x2 v = ld_nc((const u32x2*)p);
-        f.w[0] = v[0];
-        f.w[1] = v[1];
-    } else {
-        static_assert(BITS == 2, "16-channel fields need an even bit width");
-        f.w[0] = ld_nc(p);
-    }
-}
-
-// The LC codes of a field as fp32 values (code i at bits BITS*i).
-template <int BITS, int LC>
-__device__ __forceinline__ void field_values(const FieldWords<BITS, LC>& f, float (&q)[LC]) {
-    if constexpr (LC == 32) {
-        CodeWords<BITS> c;
-#pragma unroll
-        for (int i = 0; i < BITS; ++i) c.w[i] = f.w[i];
-        field_codes<BITS>(c, q);
-    } else if constexpr (BITS == 4) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t lo = f.w[i] & 0x0F0F0F0Fu, hi = (f.w[i] >> 4) & 0x0F0F0F0Fu;
-            q[8 * i + 0] = cvt_ubyte<0>(lo);
-            q[8 * i + 1] = cvt_ubyte<0>(hi);
-            q[8 * i + 2] = cvt_ubyte<1>(lo);
-            q[8 * i + 3] = cvt_ubyte<1>(hi);
-            q[8 * i + 4] = cvt_ubyte<2>(lo);
-            q[8 * i + 5] = cvt_ubyte<2>(hi);
-            q[8 * i + 6] = cvt_ubyte<3>(lo);
-            q[8 * i + 7] = cvt_ubyte<3>(hi);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t m = (f.w[0] >> (2 * j)) & 0x03030303u;   // codes 4 b + j
-            q[j] = cvt_ubyte<0>(m);
-            q[4 + j] = cvt_ubyte<1>(m);
-            q[8 + j] = cvt_ubyte<2>(m);
-            q[12 + j] = cvt_ubyte<3>(m);
-        }
-    }
-}
-
-template <int BITS, int SG, int LC>
+template <int BITS, int SG>
 struct RowField {
-    FieldWords<BITS, LC> cw;
+    CodeWords<BITS> cw;
     uint16_t dh[SG], zh[SG];
 };
 
 // Prompt p = blockIdx.y of a batched call reads X + p * x, s + p * s, ...
 // (element strides; all zero for one prompt).
-template <int BITS, int GROUP, bool XF32, bool YF32, int TT, int LC>
-__global__ __launch_bounds__(tmaxwaves(LC) * kWave) void k_qgemv_t(
+template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
+__global__ __launch_bounds__(kTMaxWaves * kWave) void k_qgemv_t(
     const void* __restrict__ X, int64_t T, int64_t K, int64_t ldx, const float* __restrict__ s,
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
     const uint16_t* __restrict__ zero, int64_t M, void* __restrict__ Y, int64_t ldy, QgemvBatch bt) {
     constexpr int RW = trows(TT);
     constexpr int D = tdepth(TT);
-    constexpr int SG = GROUP < LC ? LC / GROUP : 1;           // groups per lane field
-    constexpr int SGC = LC / SG;                              // channels per group part
+    constexpr int SG = GROUP < kTChan ? kTChan / GROUP : 1;   // groups per lane field
+    constexpr int SGC = kTChan / SG;                          // channels per group part
     constexpr int NV = RW * TT;
-    __shared__ float red[tmaxwaves(LC)][NV];
+    __shared__ float red[kTMaxWaves][NV];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int NS = blockDim.x / kWave;
     const int64_t o0 = (int64_t)blockIdx.x * RW;
     const int64_t wpr = K * BITS / 32, gpr = K / GROUP;
-    const int64_t npieces = (K + tpiece(LC) - 1) / tpiece(LC);
+    const int64_t npieces = (K + kTPiece - 1) / kTPiece;
     {
         const int64_t pb = blockIdx.y;
         X = XF32 ? (const void*)((const float*)X + pb * bt.x) : (const void*)((const uint16_t*)X + pb * bt.x);
@@ -399,11 +336,11 @@ __global__ __launch_bounds__(tmaxwaves(LC) * kWave) void k_qgemv_t(
         for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
 
     for (int64_t p = wave; p < npieces; p += NS) {
-        const int64_t k0 = p * tpiece(LC) + (int64_t)lane * LC;
-        if (k0 < K) {                             // K % LC == 0: a field is all in or all out
-            auto load_row = [&](RowField<BITS, SG, LC>& f, int r) __attribute__((always_inline)) {
+        const int64_t k0 = p * kTPiece + (int64_t)lane * kTChan;
+        if (k0 < K) {                             // K % 32 == 0: a field is all in or all out
+            auto load_row = [&](RowField<BITS, SG>& f, int r) __attribute__((always_inline)) {
                 const int64_t o = o0 + r < M ? o0 + r : M - 1;
-                load_field<BITS, LC>(f.cw, codes + o * wpr + k0 * BITS / 32);
+                load_codes<BITS>(f.cw, codes + o * wpr + k0 * BITS / 32);
 #pragma unroll
                 for (int h = 0; h < SG; ++h) {
                     f.dh[h] = scale[o * gpr + k0 / GROUP + h];
@@ -415,10 +352,10 @@ __global__ __launch_bounds__(tmaxwaves(LC) * kWave) void k_qgemv_t(
             // the first D rows.  fp32 tokens with four token slots are fetched
             // after the rows, one token at a time, to bound registers.
             constexpr bool kEarlyX = !(XF32 && TT == 4);
-            constexpr int XW = XF32 ? LC : LC / 2;             // 32-bit words per token field
-            float sv[LC];
+            constexpr int XW = XF32 ? kTChan : kTChan / 2;     // 32-bit words per token field
+            float sv[kTChan];
 #pragma unroll
-            for (int v = 0; v < LC / 4; ++v) {
+            for (int v = 0; v < kTChan / 4; ++v) {
                 const f32x4 a = *(const f32x4*)(s + k0 + 4 * v);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[4 * v + e] = a[e];
@@ -438,21 +375,21 @@ __global__ __launch_bounds__(tmaxwaves(LC) * kWave) void k_qgemv_t(
 #pragma unroll
                 for (int t = 0; t < TT; ++t) load_x(xr[t], t);
             }
-            RowField<BITS, SG, LC> ring[D];
+            RowField<BITS, SG> ring[D];
 #pragma unroll
             for (int r = 0; r < D; ++r) load_row(ring[r], r);
             __builtin_amdgcn_sched_barrier(0);              // all D rows requested before any wait
 
             // xs = x * (1/s) and its sums over each group part.
 #pragma unroll
-            for (int i = 0; i < LC; ++i) sv[i] = __builtin_amdgcn_rcpf(sv[i]);
-            float xs[TT][LC], S[TT][SG];
+            for (int i = 0; i < kTChan; ++i) sv[i] = __builtin_amdgcn_rcpf(sv[i]);
+            float xs[TT][kTChan], S[TT][SG];
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
                 if constexpr (!kEarlyX) load_x(xr[0], t);
                 const uint32_t(&xt)[XW] = xr[kEarlyX ? t : 0];
 #pragma unroll
-                for (int i = 0; i < LC; ++i) {
+                for (int i = 0; i < kTChan; ++i) {
                     float x;
                     if constexpr (XF32) x = __builtin_bit_cast(float, xt[i]);
                     else x = (i & 1) ? bf16hi_to_f32(xt[i / 2]) : bf16lo_to_f32(xt[i / 2]);
@@ -471,10 +408,10 @@ __global__ __launch_bounds__(tmaxwaves(LC) * kWave) void k_qgemv_t(
             // before row r is computed.
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                const RowField<BITS, SG, LC> f = ring[r % D];
+                const RowField<BITS, SG> f = ring[r % D];
                 if (r + D < RW) load_row(ring[r % D], r + D);
-                float q[LC];
-                field_values<BITS, LC>(f.cw, q);
+                float q[kTChan];
+                field_codes<BITS>(f.cw, q);
 #pragma unroll
                 for (int h = 0; h < SG; ++h) {
                     const float df = f16_to_f32(f.dh[h]), zf = f16_to_f32(f.zh[h]);
@@ -542,15 +479,12 @@ template <int BITS, int GROUP, bool XF32, bool YF32, int TT>
 static hipError_t launch_t(const void* X, int64_t T, int64_t K, int64_t ldx, const float* s,
                            const uint32_t* codes, const uint16_t* scale, const uint16_t* zero, int64_t M, void* Y,
                            int64_t ldy, hipStream_t st, StageTimer tm, int64_t P, const QgemvBatch& bt) {
-    // One token at even b: 16-channel lane fields (bitwise the same for every
-    // call of the same shape, batched or not).
-    constexpr int LC = (TT == 1 && BITS % 2 == 0) ? 16 : 32;
-    const int64_t np = (K + tpiece(LC) - 1) / tpiece(LC);
-    const int64_t rounds = (np + tmaxwaves(LC) - 1) / tmaxwaves(LC);
+    const int64_t np = (K + kTPiece - 1) / kTPiece;
+    const int64_t rounds = (np + kTMaxWaves - 1) / kTMaxWaves;
     const int ns = (int)((np + rounds - 1) / rounds);           // waves, each taking `rounds` pieces
     const dim3 grid((unsigned)((M + trows(TT) - 1) / trows(TT)), (unsigned)P);
-    return launch_kernel(k_qgemv_t<BITS, GROUP, XF32, YF32, TT, LC>, grid, dim3(ns * kWave), 0, st, tm.start,
-                         tm.stop, X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, bt);
+    return launch_kernel(k_qgemv_t<BITS, GROUP, XF32, YF32, TT>, grid, dim3(ns * kWave), 0, st, tm.start, tm.stop,
+                         X, T, K, ldx, s, codes, scale, zero, M, Y, ldy, bt);
 }
 
 // ---------------------------------------------------------------------------
