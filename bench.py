@@ -7,7 +7,7 @@ A step is one pass of the whole per-prompt path for one linear layer —
 activation statistics -> shrunk AWQ scales -> group RTN of the scaled weight
 -> quantized projection (plus the low-rank term when the workload has one) —
 through the C ABI's ttq_linear, on synthetic inputs already resident in HBM.
-Inputs rotate over several copies (>= 768 MiB in total) so that successive
+Inputs rotate over several copies (>= 1 GiB in total) so that successive
 steps do not find X and W in the 256 MiB Infinity Cache.
 
 By default the 4096->4096, T = 2048 layer is the headline (the JSON line's
@@ -422,7 +422,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="all",
                     help="all (default: c2 as the headline, then c1, c3, c4, c5) or one of c1..c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--min-rotation-mib", type=int, default=768)
+    ap.add_argument("--min-rotation-mib", type=int, default=1024)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for HBM counter scaling)")
     args = ap.parse_args(argv)
