@@ -61,4 +61,24 @@ __device__ __forceinline__ T ld_nc(const T* p) {
     return __builtin_nontemporal_load(p);
 }
 
+// Store, with the nontemporal (streaming) hint when NT.  A compile-time
+// choice: behind a runtime branch the compiler merges the two stores into
+// one plain store.
+template <bool NT, typename T>
+__device__ __forceinline__ void st_nt(T* p, const T& v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Streaming stores for a staged dequantized weight (and its codes) larger
+// than this.  Measured on MI355X: with a 117 MB w~ (4096 x 14336 or 14336 x
+// 4096 bf16) ordinary stores leave the Infinity Cache (256 MiB, also holding
+// the weight being read) full of dirty lines that the projection then
+// competes with (4096 -> 14336, T = 512: layer 135.9 -> 126.4-127.2 us with
+// streaming stores; 14336 -> 4096, T = 1024: 189.5 -> 183.4-185.2 us); a
+// 33.5 MB w~ (4096 x 4096) is read back from that cache by the projection,
+// and streaming it cost ~1 us.
+constexpr int64_t kStreamStageBytes = (int64_t)64 << 20;
+inline bool stream_stage(int64_t M, int64_t K) { return M * K * 2 > kStreamStageBytes; }
+
 }  // namespace ttq

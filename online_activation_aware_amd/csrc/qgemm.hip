@@ -217,8 +217,9 @@ __global__ __launch_bounds__(kGThreads) void k_qgemm(
 // exact in fp32; 1/s by v_rcp_f32; one RNE rounding), written densely as
 // [M][K] bf16 for the matrix-core GEMM.  One thread per 8 codes: the codes
 // are read as whole dwords, the 8 weights stored as one 16-byte vector.
-// Grid: x over the K/8 units of a row, y over rows (grid-strided).
-template <int BITS, int GROUP>
+// Grid: x over the K/8 units of a row, y over rows (grid-strided).  A w~
+// larger than 64 MiB is written by streaming stores (stream_stage).
+template <int BITS, int GROUP, bool NT>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
                                                  const uint16_t* __restrict__ scale,
                                                  const uint16_t* __restrict__ zero,
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
         const int64_t gi = o * gpr + col / GROUP;
         WUnit<BITS, false> w;
         dequant_unit<BITS, false>(f, f16_to_f32(zero[gi]), f16_to_f32(scale[gi]), inv, w);
-        *(u32x4*)(wq + o * K + col) = w.hi;
+        st_nt<NT>((u32x4*)(wq + o * K + col), w.hi);
     }
 }
 
@@ -250,9 +251,12 @@ static hipError_t launch_g3(const void* X, bool xf32, int64_t T, int64_t K, int6
                             uint16_t* wq, hipStream_t st, StageTimer tm) {
     if (wq != nullptr) {
         dim3 gd((unsigned)((K / 8 + 255) / 256), (unsigned)(M < 8192 ? M : 8192));
-        if (hipError_t e = launch_kernel(k_dequant<BITS, GROUP>, gd, dim3(256), 0, st, tm.start, nullptr, codes,
-                                         scale, zero, s, M, K, wq))
-            return e;
+        hipError_t e = stream_stage(M, K)
+                           ? launch_kernel(k_dequant<BITS, GROUP, true>, gd, dim3(256), 0, st, tm.start, nullptr,
+                                           codes, scale, zero, s, M, K, wq)
+                           : launch_kernel(k_dequant<BITS, GROUP, false>, gd, dim3(256), 0, st, tm.start, nullptr,
+                                           codes, scale, zero, s, M, K, wq);
+        if (e != hipSuccess) return e;
         return launch_gemm_bf16((const uint16_t*)X, T, K, ldx, wq, K, M, Y, yf32, ldy, st, {nullptr, tm.stop},
                                 nullptr, split_ws_after(wq, M, K));
     }

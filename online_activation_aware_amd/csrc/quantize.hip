@@ -38,7 +38,10 @@
 // (QDQ) with the input scale folded back, w~ = bf16(((code - zero) * step) *
 // (1/s)), dense [M][K] bf16: the operand of the prompt-sized projection, so
 // that the codes need not be read and expanded a second time.  (code - zero)
-// comes out exactly as sum - (1.5 * 2^23 + zero).
+// comes out exactly as sum - (1.5 * 2^23 + zero).  A w~ larger than 64 MiB
+// is written, with the codes of even bit widths (whole 4- or 8-byte fields
+// per lane), by streaming stores (stream_stage); the single-word code stores
+// of odd widths measured slower streamed.
 #include <atomic>
 
 #include "common.hpp"
@@ -96,7 +99,7 @@ __device__ __forceinline__ LaneField<BITS> pack_lane(const uint32_t (&qb)[kLaneC
 // Group RTN of one lane's 16 values and the stores of its codes, step, zero
 // and (optionally) dequantized weights.  All 64 lanes of the wave must call
 // this together (cross-lane moves).
-template <int BITS, int GROUP>
+template <int BITS, int GROUP, bool NT>
 __device__ __forceinline__ void quantize_and_store(const float (&v)[kLaneCh], bool active, int lane, int64_t cu,
                                                    int64_t col, int64_t o, int64_t words_per_row,
                                                    int64_t groups_per_row, uint32_t* __restrict__ codes,
@@ -130,8 +133,8 @@ __device__ __forceinline__ void quantize_and_store(const float (&v)[kLaneCh], bo
                                  ((qm[9 + 2 * p] - mz) * g.df) * sinv[9 + 2 * p]);
         }
         u32x4* dst = (u32x4*)(wq + o * K + col);
-        dst[0] = pk0;
-        dst[1] = pk1;
+        st_nt<NT>(dst, pk0);
+        st_nt<NT>(dst + 1, pk1);
     }
 
     const LaneField<BITS> f = pack_lane<BITS>(qb);
@@ -140,10 +143,10 @@ __device__ __forceinline__ void quantize_and_store(const float (&v)[kLaneCh], bo
         if (active) {
             uint32_t* wrow = codes + o * words_per_row + cu * (BITS / 2);
             if constexpr (BITS == 2) {
-                wrow[0] = f.w[0];
+                st_nt<NT>(wrow, f.w[0]);
             } else {
                 u32x2 pr = {f.w[0], f.w[1]};
-                *(u32x2*)wrow = pr;
+                st_nt<NT>((u32x2*)wrow, pr);
             }
         }
     } else {
@@ -174,7 +177,7 @@ __device__ __forceinline__ void quantize_and_store(const float (&v)[kLaneCh], bo
             // even lane: the first NW words, odd lane: the remaining BITS - NW
 #pragma unroll
             for (int k = 0; k < BITS; ++k)
-                if ((k < NW) == even) wrow[k] = pair[k];
+                if ((k < NW) == even) wrow[k] = pair[k];   // single words: plain stores
         }
     }
     if (active && (cu % GL) == 0) {
@@ -235,7 +238,7 @@ __device__ __forceinline__ void unpack_row(const RawRow<WF32>& r, float (&w)[kLa
     }
 }
 
-template <int BITS, int GROUP, bool WF32, bool SFUSE>
+template <int BITS, int GROUP, bool WF32, bool SFUSE, bool NT>
 __global__ __launch_bounds__(kQThreads) void k_quantize(
     const void* __restrict__ W, int64_t M, int64_t K, int64_t ldw, const float* __restrict__ s,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero,
@@ -333,8 +336,8 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(
             float v[kLaneCh];
 #pragma unroll
             for (int i = 0; i < kLaneCh; ++i) v[i] = wv[i] * sc[i];
-            quantize_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row, codes,
-                                            scale, zero, sinv, wq, K);
+            quantize_and_store<BITS, GROUP, NT>(v, active, lane, cu, col, o, words_per_row, groups_per_row, codes,
+                                                scale, zero, sinv, wq, K);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) cur[r] = nxt[r];
@@ -376,23 +379,27 @@ static hipError_t launch_q3(const void* W, bool wf32, int64_t M, int64_t K, int6
     const int rpb = wf32 ? 8 : 16;                // rows per block: 4 waves x RB
     const int64_t nrb = (M + rpb - 1) / rpb;
     const QScaleSrc q = qs ? *qs : QScaleSrc{};
+    const int wnt = wq != nullptr && stream_stage(M, K);   // streaming stores for a large staged w~
     // Persistent row loop over as many workgroups as the device holds at
     // once.  The residency of each kernel instantiation is memoized per
     // device: a value the runtime derives from the code object, the same on
     // every call, so the memo never changes a result.
-#define TTQ_Q_LAUNCH(WF, SF)                                                                               \
+#define TTQ_Q_LAUNCH(WF, SF, NT)                                                                           \
     do {                                                                                                   \
         static OccMemo memo;                                                                               \
-        auto kern = k_quantize<BITS, GROUP, WF, SF>;                                                       \
+        auto kern = k_quantize<BITS, GROUP, WF, SF, NT>;                                                   \
         const int64_t gy = persistent_rows_grid(resident_workgroups((const void*)kern, kQThreads, 0, memo, 0), \
                                                 strips, nrb);                                              \
         return launch_kernel(kern, dim3((unsigned)strips, (unsigned)gy), dim3(kQThreads), 0, st, tm.start, \
                              tm.stop, W, M, K, ldw, s, codes, scale, zero, wq, q);                         \
     } while (0)
+    // Streaming stores are instantiated for bf16 weights only.
     if (wf32) {
-        if (qs) TTQ_Q_LAUNCH(true, true); else TTQ_Q_LAUNCH(true, false);
+        if (qs) TTQ_Q_LAUNCH(true, true, false); else TTQ_Q_LAUNCH(true, false, false);
+    } else if (wnt) {
+        if (qs) TTQ_Q_LAUNCH(false, true, true); else TTQ_Q_LAUNCH(false, false, true);
     } else {
-        if (qs) TTQ_Q_LAUNCH(false, true); else TTQ_Q_LAUNCH(false, false);
+        if (qs) TTQ_Q_LAUNCH(false, true, false); else TTQ_Q_LAUNCH(false, false, false);
     }
 #undef TTQ_Q_LAUNCH
 }

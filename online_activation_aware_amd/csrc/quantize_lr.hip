@@ -75,7 +75,7 @@ __device__ __forceinline__ void unpack_row8(const RawRow8<WF32>& r, double (&w)[
 // Group RTN of one lane's 8 values and the stores of the quad's 32 codes,
 // the step and zero, and (optionally) the dequantized weights.  All 64 lanes
 // of the wave must call this together (cross-lane moves).
-template <int BITS, int GROUP>
+template <int BITS, int GROUP, bool NT>
 __device__ __forceinline__ void quantize8_and_store(const float (&v)[kLrLaneCh], bool active, int lane, int64_t cu,
                                                     int64_t col, int64_t o, int64_t words_per_row,
                                                     int64_t groups_per_row, uint32_t* __restrict__ codes,
@@ -104,7 +104,7 @@ __device__ __forceinline__ void quantize8_and_store(const float (&v)[kLrLaneCh],
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             pk[p] = pack_bf16x2(((qm[2 * p] - mz) * g.df) * sinv[2 * p], ((qm[2 * p + 1] - mz) * g.df) * sinv[2 * p + 1]);
-        *(u32x4*)(wq + o * K + col) = pk;
+        st_nt<NT>((u32x4*)(wq + o * K + col), pk);
     }
 
     // Quad assembly: lanes 4m..4m+3 hold 32 codes = BITS words; every lane
@@ -137,7 +137,7 @@ __device__ __forceinline__ void quantize8_and_store(const float (&v)[kLrLaneCh],
     if (active) {
         const int j = lane & 3;
         uint32_t* wrow = codes + o * words_per_row + (cu >> 2) * BITS;
-        if (j < BITS) wrow[j] = word(j);
+        if (j < BITS) wrow[j] = word(j);                   // single words: plain stores
         if (BITS > 4 && j == 0) wrow[4] = word(4);
         if ((cu % GL) == 0) {
             const int64_t gi = o * groups_per_row + col / GROUP;
@@ -147,7 +147,7 @@ __device__ __forceinline__ void quantize8_and_store(const float (&v)[kLrLaneCh],
     }
 }
 
-template <int BITS, int GROUP, bool WF32, bool SFUSE>
+template <int BITS, int GROUP, bool WF32, bool SFUSE, bool NT>
 __global__ __launch_bounds__(kLrThreads) void k_quantize_lr(
     const void* __restrict__ W, int64_t M, int64_t K, int64_t ldw, const float* __restrict__ s,
     const float* __restrict__ B, const float* __restrict__ A, int rank, uint32_t* __restrict__ codes,
@@ -299,8 +299,8 @@ __global__ __launch_bounds__(kLrThreads) void k_quantize_lr(
             float v[kLrLaneCh];
 #pragma unroll
             for (int i = 0; i < kLrLaneCh; ++i) v[i] = (float)(acc[r][i] * (double)sc[i]);
-            quantize8_and_store<BITS, GROUP>(v, active, lane, cu, col, o, words_per_row, groups_per_row, codes,
-                                             scale, zero, sinv, wq, K);
+            quantize8_and_store<BITS, GROUP, NT>(v, active, lane, cu, col, o, words_per_row, groups_per_row, codes,
+                                                 scale, zero, sinv, wq, K);
         }
 #pragma unroll
         for (int r = 0; r < kLrRB; ++r) cur[r] = nxt[r];
@@ -316,20 +316,24 @@ static hipError_t launch_lr3(const void* W, bool wf32, int64_t M, int64_t K, int
     const int lds_ranks = rank < kLrLdsRanks ? rank : kLrLdsRanks;
     const size_t lds = (size_t)((lds_ranks + kLrChunk - 1) / kLrChunk * kLrChunk) * kLrChans * sizeof(float);
     const QScaleSrc q = qs ? *qs : QScaleSrc{};
-#define TTQ_LR_LAUNCH(WF, SF)                                                                                  \
+    const int wnt = wq != nullptr && stream_stage(M, K);   // streaming stores for a large staged w~
+#define TTQ_LR_LAUNCH(WF, SF, NT)                                                                              \
     do {                                                                                                       \
         static OccMemo memo;                                                                                   \
-        auto kern = k_quantize_lr<BITS, GROUP, WF, SF>;                                                        \
+        auto kern = k_quantize_lr<BITS, GROUP, WF, SF, NT>;                                                    \
         const int64_t gy = persistent_rows_grid(resident_workgroups((const void*)kern, kLrThreads, lds, memo,     \
                                                                     lds_ranks),                                \
                                                 strips, nrb);                                                  \
         return launch_kernel(kern, dim3((unsigned)strips, (unsigned)gy), dim3(kLrThreads), lds, st, tm.start,   \
                              tm.stop, W, M, K, ldw, s, B, A, rank, codes, scale, zero, wq, q);                 \
     } while (0)
+    // Streaming stores are instantiated for bf16 weights only.
     if (wf32) {
-        if (qs) TTQ_LR_LAUNCH(true, true); else TTQ_LR_LAUNCH(true, false);
+        if (qs) TTQ_LR_LAUNCH(true, true, false); else TTQ_LR_LAUNCH(true, false, false);
+    } else if (wnt) {
+        if (qs) TTQ_LR_LAUNCH(false, true, true); else TTQ_LR_LAUNCH(false, false, true);
     } else {
-        if (qs) TTQ_LR_LAUNCH(false, true); else TTQ_LR_LAUNCH(false, false);
+        if (qs) TTQ_LR_LAUNCH(false, true, false); else TTQ_LR_LAUNCH(false, false, false);
     }
 #undef TTQ_LR_LAUNCH
 }
