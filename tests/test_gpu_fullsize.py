@@ -95,6 +95,19 @@ def test_fullsize_linear(T, key):
     worst = y_elementwise_check(Yh, d["X"], wl.xdtype, s, q_all, d16, z16, wl.group, B, A)
     say(f"  Y element-wise: worst |error| / bound {worst:.3f}")
 
+    if not wl.rank and wl.xdtype == "bf16" and wl.M * wl.K * 2 > 64 << 20:
+        # The prompt projected again from the stored state through ttq_qgemm:
+        # its dequantize kernel writes w~ with streaming stores at this size
+        # (like the quantizer inside ttq_linear), with the same arithmetic, and
+        # the same GEMM runs, so Y must be bitwise the same.
+        ws_p = T.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group)
+        Yq = T.ttq_qgemm(to_dev(d["X"], wl.xdtype), st["s"], st["codes"], st["scale_f16"], st["zero_f16"],
+                         wl.M, wl.bits, wl.group, ws=ws_p)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Yq), Yh), "ttq_qgemm on the stored state differs from ttq_linear"
+        say("  ttq_qgemm on the stored state: bitwise equal to ttq_linear")
+        del Yq, ws_p
+
     if wl.decode_T:
         ws = T.workspace(max(wl.decode_T), wl.K, wl.M, wl.bits, wl.group)
         for td, Xd in d["X_decode"].items():
