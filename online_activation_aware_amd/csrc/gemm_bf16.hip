@@ -16,8 +16,8 @@
 // registers); 128-byte LDS rows with an XOR chunk swizzle (conflict-free);
 // one barrier per 64-deep K step, each wave waiting only for its own DMA.
 // Fragments are double-buffered in registers: the LDS reads of one 32-deep
-// half overlap the MFMAs of the other, and waves raise their issue priority
-// while they feed the matrix cores.
+// half overlap the MFMAs of the other.  (Raising the wave priority around the
+// MFMA phases measured ~0.3 us slower on the 4096 x 4096, T = 2048 layer.)
 // Optionally the epilogue adds the low-rank term Z B^T (fp32, rank <= 64)
 // before the store.
 #include <algorithm>
@@ -121,12 +121,10 @@ __global__ __launch_bounds__(kBThreads, 1) void k_gemm_bf16(
         for (int j = 0; j < FB; ++j) b[j] = *(const u32x4*)(xs + lds_swz(wn * WT + 16 * j + (lane & 15), c));
     };
     auto mm = [&](const u32x4* a, const u32x4* b) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < FB; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
-        __builtin_amdgcn_s_setprio(0);
     };
     // Step kt (ring slot xc/wc): its first-half fragments are read while the
     // previous step's second half runs on the matrix cores; then the DMA two
