@@ -46,7 +46,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 # invalidates them (traffic is then reported as null).
 MEASURED_TRAFFIC = {
     # 4096->4096, T=2048 layer: profiles/ttq_linear_4096x4096_t2048_b4g32_pmc_traffic.txt
-    "aa9fbc3ea2ca3f9f": {"workload": "c2", "fetch_bytes": 134378945, "write_bytes": 35478938,
+    "6c1ab95eb15a86b8": {"workload": "c2", "fetch_bytes": 134378945, "write_bytes": 35414221,
                          "fetch_factor": 1.9999, "write_factor": 1.0},
 }
 

@@ -232,7 +232,9 @@ bool gemm_bf16_supported(int64_t T, int64_t K, int64_t ldx, int64_t ldw) {
 }
 
 // Y = P[0] + P[1] + ... (fp32 partial products of the K slices, added in
-// slice order, rows of ldp floats), stored as fp32 or bf16 (RNE).
+// slice order, rows of ldp floats), stored as fp32 or bf16 (RNE).  The
+// partials are read with the nontemporal hint: they are dead afterwards
+// (14336 -> 4096, T = 1024: layer 184.8 -> 181.9 us).
 template <bool YF32>
 __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ P, int S, int64_t T, int64_t M,
                                                    int64_t ldp, int64_t zstride, void* __restrict__ Y, int64_t ldy,
@@ -240,9 +242,9 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ P, 
     const int64_t nq = (M + 3) / 4;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * nq; i += (int64_t)gridDim.x * 256) {
         const int64_t t = i / nq, o = 4 * (i % nq);
-        f32x4 acc = *(const f32x4*)(P + t * ldp + o);
+        f32x4 acc = ld_nc((const f32x4*)(P + t * ldp + o));
         for (int s = 1; s < S; ++s) {
-            const f32x4 v = *(const f32x4*)(P + s * zstride + t * ldp + o);
+            const f32x4 v = ld_nc((const f32x4*)(P + s * zstride + t * ldp + o));
             acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
         }
         store_y4<YF32>(Y, t * ldy + o, M - o, yvec, acc);
