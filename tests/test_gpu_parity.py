@@ -569,6 +569,36 @@ def test_linear_lowrank_unaligned_factor(T):
     assert rel_fro(host(Y2), host(Y)) < 1e-5
 
 
+def test_linear_lowrank_streamed_stage(T):
+    # A residual layer whose staged w~ exceeds 64 MiB (8192 x 4608 bf16,
+    # 75.5 MB): the residual quantizer writes w~ by streaming stores.  Its
+    # codes, steps and zeros must equal the standalone quantizer's (which
+    # stages nothing) bit for bit; Y must equal the projection of that state
+    # plus the low-rank term, and the oracle on sampled rows.
+    say("linear low-rank, streamed w~ (8192 x 4608, rank 8)")
+    wl, d = _inputs("c5", T=256, K=4608, M=8192)
+    rng = np.random.default_rng(7)
+    B = (rng.standard_normal((wl.M, 8)) * 0.02).astype(np.float32)
+    A = (rng.standard_normal((8, wl.K)) * 0.02).astype(np.float32)
+    Y, st = _run_linear(T, wl, d, B, A)
+    dev_w = to_dev(d["W"], wl.wdtype)
+    codes, scale, zero = T.ttq_quantize_groups(dev_w, st["s"], wl.bits, wl.group, B=f32_dev(B), A=f32_dev(A))
+    assert torch.equal(codes, st["codes"])
+    assert torch.equal(scale.view(torch.int16), st["scale_f16"].view(torch.int16))
+    assert torch.equal(zero.view(torch.int16), st["zero_f16"].view(torch.int16))
+    dev_x = to_dev(d["X"], wl.xdtype)
+    ws = T.workspace(wl.T, wl.K, wl.M, wl.bits, wl.group, rank=8)
+    Yq = T.ttq_qgemm(dev_x, st["s"], st["codes"], st["scale_f16"], st["zero_f16"], wl.M, wl.bits, wl.group, ws=ws)
+    T.ttq_lowrank_add(dev_x, f32_dev(A), f32_dev(B), Yq, ws=ws)
+    assert rel_fro(host(Yq), host(Y)) < 1e-5
+    rows = np.array([0, 1, 2047, 4096, 6000, wl.M - 1])
+    ref = oracle.linear(d["X"], wl.xdtype, d["W"], wl.wdtype, wl.bits, wl.group, wl.alpha, wl.lambda_rel,
+                        B=B, A=A, rows=rows)
+    err = rel_fro(host(Y)[:, rows], ref["Y"])
+    say(f"  Y rel err (sampled rows) {err:.3e}")
+    assert err < Y_TOL
+
+
 def test_decode_steps_reuse_prompt_state(T):
     say("decode steps")
     wl, d = _inputs("c4", T=64, K=2048, M=256, decode_T=(1, 4, 16))
